@@ -1,0 +1,30 @@
+"""CPU oracle for the W4A16 speculative-verify path -- TEST INFRASTRUCTURE ONLY.
+
+Plain, slow, fp64 numpy definitions of what the verify step computes.  Only
+``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import it; the product path (the HIP library and its Python
+binding) never does, and this package never imports the product path.  The
+two sides share nothing but the seeded input module ``gen``.
+
+Sources (organisers' page "Efficient LLM Challenge Results", adaptfm.gitlab.io):
+  section 3  -- speculative decoding: K drafts verified in one target pass,
+                keep the longest prefix the target would itself produce;
+                greedy serving; the winner's target is W4A16 GPTQ with group
+                size 128 and an untied lm_head quantised to 8 bits; the
+                runner-up pads drafts to K=20 with -1 sentinels, and a padded
+                position is accepted only if it equals the target's greedy token.
+  section 5  -- W4A16 (group size 128), W8A16 lm_head.
+
+Modules:
+  quant   -- int4 unpacking and group dequantisation
+  gemm    -- the W4A16 linear and fp16 storage rounding
+  lmhead  -- 8-bit lm_head logits, argmax with tie-break, top-2 margin
+  verify  -- greedy prefix acceptance with sentinels, verified-token count
+  step    -- the free-running verify step (chain of linears, lm_head, verify)
+
+Every function is pinned by a ``-m "not gpu"`` test (pack/unpack round trips,
+hand-built words, identity and one-hot weights, closed forms, exact-rational
+brute force on tiny shapes, exhaustive enumeration for the verify).  No
+function here is "parity unpinned".
+"""
+from . import quant, gemm, lmhead, verify, step  # noqa: F401

@@ -1,0 +1,49 @@
+"""8-bit lm_head, greedy argmax and top-2 margin (oracle; test infrastructure only).
+
+Results page, section 3: the winning target keeps its lm_head untied and
+quantised to 8 bits and serves greedily (temperature 0); section 5 names a
+W8A16 lm_head.  Readings: symmetric per-output-channel quantisation with no
+zero-point, int8 weights [V, H] row-major and one fp16 scale per vocabulary
+row; logits are never rounded to 16 bits; ties go to the lowest index.
+"""
+import numpy as np
+
+_CHUNK = 8192   # vocabulary rows per slice; bounds memory only
+
+
+def logits(h, w8, s8) -> np.ndarray:
+    """fp64 [M, V]: L[m, v] = s8[v] * sum_h H[m, h] * q8[v, h]."""
+    h64 = np.asarray(h).astype(np.float64)
+    w8 = np.asarray(w8)
+    s64 = np.asarray(s8).astype(np.float64)
+    v = w8.shape[0]
+    out = np.empty((h64.shape[0], v), dtype=np.float64)
+    for lo in range(0, v, _CHUNK):
+        hi = min(v, lo + _CHUNK)
+        out[:, lo:hi] = (h64 @ w8[lo:hi].astype(np.float64).T) * s64[None, lo:hi]
+    return out
+
+
+def argmax_margin(lg: np.ndarray):
+    """Per row: (t, top, margin).
+
+    t[m]      = lowest v with L[m, v] equal to the row maximum;
+    top[m]    = L[m, t[m]];
+    margin[m] = top[m] - max over v != t[m] of L[m, v] (0 on an exact tie).
+    """
+    lg = np.asarray(lg, dtype=np.float64)
+    m = lg.shape[0]
+    t = np.argmax(lg, axis=1)          # first occurrence of the maximum
+    rows = np.arange(m)
+    top = lg[rows, t]
+    if lg.shape[1] == 1:
+        return t.astype(np.int64), top, np.full(m, np.inf)
+    rest = lg.copy()
+    rest[rows, t] = -np.inf
+    margin = top - rest.max(axis=1)
+    return t.astype(np.int64), top, margin
+
+
+def lmhead_argmax(h, w8, s8):
+    """(target ids, max logits, margins) for the rows of ``h``."""
+    return argmax_margin(logits(h, w8, s8))
