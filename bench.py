@@ -1,0 +1,231 @@
+"""Benchmark: one speculative-decoding verify step on one MI355X.
+
+Workload (the verify step at M = 16, K = 15):
+  36 synthetic 4B-class layers x 4 W4A16 group-128 linears
+  (2560->6144, 4096->2560, 2560->19456, 9728->2560) at M = 16 rows,
+  an int8 lm_head 2560 -> 151,936 with fused per-row argmax, and greedy
+  verification of 15 drafts whose accepted length is min(15, Geometric(0.25)).
+A step = all 144 linears + the fused lm_head/argmax/verify launch, replayed
+from a HIP graph; new drafts are copied in before every step.  All inputs
+are seeded synthetic tensors already resident in HBM.
+
+Prints ONE JSON line (rank 0).  ``value`` is the step's algorithmic HBM
+throughput in GB/s (bytes the step must read and write, divided by the
+measured step time); verified tokens/s and the linears' own GB/s ride along.
+``roofline`` covers the dominant kernel (the W4A16 linear): its algorithmic
+bytes per launch over its average launch duration, timed with HIP events
+on the stream it runs on.  ``cpu_baseline`` times the numpy oracle on a
+bounded sample of the same workload on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "W4A16 verify GEMM HBM GB/s (% of peak) at M=16; verified tokens/s"
+
+
+def linear_bytes(m, k, n):
+    """Algorithmic HBM bytes of one W4A16 linear: weights, scales, zeros, x read, y written."""
+    g = k // 128
+    return k * n // 2 + g * n * 2 + g * n // 2 + m * k * 2 + m * n * 2
+
+
+def lmhead_bytes(m, h, v, k_draft):
+    return v * h + v * 2 + m * h * 2 + m * 4 + m * 4 + k_draft * 4 + 4 + m * 4
+
+
+def cpu_baseline(wl, plan, drafts, min_seconds: float = 10.0):
+    """Time the oracle on whole verify steps of the same workload (36 layers at
+    M = 16, the full lm_head, greedy verify) until ``min_seconds`` have passed."""
+    import numpy as np
+    from oracle import step as ostep
+
+    cores = min(len(os.sched_getaffinity(0)), 16)
+    steps = 0
+    t0 = time.perf_counter()
+    while True:
+        ostep.verify_step(wl.x, wl.linears, plan, wl.lm_w, wl.lm_s, drafts, 1, drafts.shape[-1],
+                          workers=cores)
+        steps += 1
+        if time.perf_counter() - t0 >= min_seconds:
+            break
+    dt = time.perf_counter() - t0
+    step_b = sum(linear_bytes(16, k, n) for k, n, _ in plan) + lmhead_bytes(16, 2560, 151936, 15)
+    gbs = step_b * steps / dt / 1e9
+    return {"value": round(gbs, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "seconds": round(dt, 2), "ms_per_step": round(1e3 * dt / steps, 1),
+            "sample": f"{steps} whole verify steps of the same workload (36 layers x 4 linears "
+                      f"at M=16, lm_head 2560->151936, greedy verify) through the numpy fp64 "
+                      f"oracle, {dt:.1f} s on {cores} threads"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--gemm-reps", type=int, default=50,
+                    help="replays of the linears-only graph for the roofline timing")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on exactly one GPU: the verify step has no multi-GPU path "
+              "in this build (sharding is described in DESIGN.md).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import gen
+    import w4a16_speculative_verify_amd as w4v
+    from w4a16_speculative_verify_amd.step import DeviceLinear, VerifyStep
+
+    w4v.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    cfg = gen.CONFIGS[3]
+    print(f"[bench] generating the seeded verify-step workload ({cfg.note})", file=sys.stderr,
+          flush=True)
+    wl = gen.make_workload(3)
+    plan = gen.chain_plan(cfg)
+
+    def up(a):
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    lins = [DeviceLinear(up(l.qweight), up(l.scales), up(l.qzeros), k, n, a)
+            for l, (k, n, a) in zip(wl.linears, plan)]
+    step = VerifyStep(lins, up(wl.lm_w), up(wl.lm_s), cfg.m, cfg.batch, cfg.k_draft)
+    x = up(wl.x)
+    torch.cuda.synchronize()
+
+    # target ids of this input (untimed), then one draft block per step
+    no_drafts = torch.full((1, cfg.k_draft), -1, dtype=torch.int32, device=dev)
+    t_ids, _, _, _ = step(x, no_drafts)
+    t_host = t_ids.cpu().numpy()
+    drng = gen.draft_rng(3)
+    total = args.warmup + args.steps
+    drafts_all = np.empty((total, 1, cfg.k_draft), dtype=np.int32)
+    planned = np.empty(total, dtype=np.int64)
+    for i in range(total):
+        drafts_all[i], r = gen.make_drafts(drng, cfg, t_host)
+        planned[i] = r[0]
+    drafts_dev = up(drafts_all)
+    drafts_buf = torch.empty((1, cfg.k_draft), dtype=torch.int32, device=dev)
+    acc_hist = torch.zeros(total, dtype=torch.int32, device=dev)
+
+    # capture: the whole step, and the linears alone (roofline timing)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step(x, drafts_buf)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g_step = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g_step):
+        step(x, drafts_buf)
+    g_lin = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g_lin):
+        step.linears_only(x)
+    torch.cuda.synchronize()
+
+    def one_step(i):
+        drafts_buf.copy_(drafts_dev[i], non_blocking=True)
+        g_step.replay()
+        acc_hist[i:i + 1].copy_(step.accepted_len, non_blocking=True)
+
+    for i in range(args.warmup):
+        one_step(i)
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for i in range(args.warmup, total):
+        one_step(i)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    step_ms = ev0.elapsed_time(ev1) / args.steps
+
+    acc = acc_hist.cpu().numpy().astype(np.int64)
+    if not np.array_equal(acc, planned):
+        print(f"[bench] accepted lengths differ from the planned ones", file=sys.stderr)
+        sys.exit(1)
+    tokens = int(np.sum(acc[args.warmup:] + 1))
+    tok_per_s = tokens / (step_ms * args.steps / 1e3)
+
+    # linears only: average launch duration of the W4A16 kernel
+    for _ in range(3):
+        g_lin.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.gemm_reps):
+        g_lin.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    lin_ms = e0.elapsed_time(e1) / args.gemm_reps
+    n_launch = len(plan)
+    lin_b = sum(linear_bytes(cfg.m, k, n) for k, n, _ in plan)
+    lm_b = lmhead_bytes(cfg.m, gen.HIDDEN, cfg.vocab, cfg.k_draft)
+    act_launch_us = lin_ms * 1e3 / n_launch
+    gemm_gbs = lin_b / (lin_ms / 1e3) / 1e9
+    step_gbs = (lin_b + lm_b) / (step_ms / 1e3) / 1e9
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(wl, plan, drafts_all[0], args.cpu_seconds)
+
+    out = {
+        "metric": METRIC,
+        "value": round(step_gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp16",
+        "data": "synthetic",
+        "config": {"workload": "verify step M=16 (K=15): 36 layers x W4A16 g128 "
+                               "(2560->6144, 4096->2560, 2560->19456, 9728->2560) + int8 "
+                               "lm_head 2560->151936 with fused argmax + greedy verify",
+                   "m": cfg.m, "layers": 36, "vocab": cfg.vocab, "k_draft": cfg.k_draft,
+                   "global_batch": cfg.batch, "parallelism": "single GPU"},
+        "pct_of_hbm_peak": round(100 * step_gbs / HBM_PEAK_GBS, 2),
+        "verified_tokens_per_s": round(tok_per_s, 1),
+        "mean_accepted_plus_one": round(tokens / args.steps, 3),
+        "gemm_gbs": round(gemm_gbs, 1),
+        "gemm_pct_of_hbm_peak": round(100 * gemm_gbs / HBM_PEAK_GBS, 2),
+        "linears_us_per_step": round(lin_ms * 1e3, 2),
+        "step_bytes": lin_b + lm_b,
+        "wall_s_timed": round(wall, 4),
+        "roofline": {"bound": "hbm", "achieved": round(gemm_gbs, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(gemm_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": None,
+                     "kernel": "w4a16_skinny_kernel<1>",
+                     "bytes_per_launch": round(lin_b / n_launch),
+                     "avg_launch_us": round(act_launch_us, 3)},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -320,6 +320,11 @@ def make_workload(cid: int, seed_offset: int = 0, m: int | None = None,
     return Workload(cfg, x, linears, lm_w, lm_s, extra, r_d)
 
 
+def draft_rng(cid: int, seed_offset: int = 0):
+    """A fresh copy of the draft stream of ``make_workload(cid, seed_offset)``."""
+    return streams(1000 * cid + seed_offset, 4)[3]
+
+
 def chain_plan(cfg: Config) -> list:
     """(k_in, n_out, alpha) for each linear in execution order.
 

@@ -1,0 +1,156 @@
+/*
+ * w4v.h -- C ABI of the W4A16 speculative-verify library (libw4v.so, gfx950).
+ *
+ * The operations follow the organisers' page "Efficient LLM Challenge
+ * Results" (adaptfm.gitlab.io/competition-results), section 3: a drafter
+ * proposes K tokens, the target verifies them in a single forward pass over
+ * the K+1 positions and keeps the longest prefix it would itself have
+ * produced; the winning target is W4A16 GPTQ with group size 128 and an
+ * untied lm_head quantised to 8 bits, served greedily; the runner-up pads
+ * every draft to a constant K=20 with -1 sentinels, accepted only when they
+ * match the target's own greedy token.  Section 5 names the W8A16 lm_head.
+ *
+ * Conventions for every call:
+ *   - Tensor pointers are DEVICE pointers owned by the caller.  The library
+ *     never allocates, frees or synchronises on these calls.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *     Calls are asynchronous and ordered on that stream.
+ *   - Arguments are validated on the host before any HIP call; a failure
+ *     returns a negative w4v_status and launches nothing.  A launch error
+ *     returns W4V_ERR_HIP.  Faults inside a kernel surface at the caller's
+ *     next synchronisation.  No C++ exception crosses this interface.
+ *   - fp16 means IEEE binary16; row-major everywhere; leading dimensions
+ *     (ld*) are in elements.
+ *   - Workspaces: size them with the *_workspace_size query and zero them
+ *     ONCE after allocation.  Kernels leave their counters at zero when they
+ *     finish, and the counters sit at the same offset for every call, so one
+ *     workspace sized for the largest call may be shared by calls of any
+ *     shape that are ordered on one stream.  Calls that overlap in time must
+ *     not share a workspace.  After a kernel fault, zero the workspace again.
+ */
+#ifndef W4V_H
+#define W4V_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define W4V_ABI_VERSION 1
+
+typedef enum {
+  W4V_OK = 0,
+  W4V_ERR_INVALID_ARG = -1,   /* null pointer, bad size, bad stride           */
+  W4V_ERR_UNSUPPORTED = -2,   /* valid request this build does not implement  */
+  W4V_ERR_ALIGNMENT = -3,     /* pointer or stride breaks a stated alignment  */
+  W4V_ERR_WORKSPACE = -4,     /* workspace missing or smaller than required   */
+  W4V_ERR_HIP = -5            /* the HIP runtime reported an error            */
+} w4v_status;
+
+/* Static English text for a status code (never NULL). */
+const char* w4v_status_string(int status);
+
+/* W4V_ABI_VERSION of the built library. */
+int w4v_abi_version(void);
+
+/* ------------------------------------------------------------------------
+ * W4A16 linear (section 3: 4-bit weights, group size 128, 16-bit activations)
+ *
+ *   y[m, n] = fp16_rne( alpha * sum_k x[m, k] * s[k/128, n] * (q[k, n] - z[k/128, n]) )
+ *
+ * x        fp16  [M x K], row stride ldx >= K; 16-byte aligned, ldx % 8 == 0.
+ * qweight  int32 [K/8 x N]: nibble j (bits 4j..4j+3) of word (i, n) is
+ *          q[8i + j][n], an unsigned 4-bit value; 16-byte aligned.
+ * scales   fp16  [K/group_size x N]; 16-byte aligned.
+ * qzeros   int32 [K/group_size x N/8]: nibble j of word (g, i) is z[g][8i + j];
+ *          4-byte aligned.
+ * y        fp16  [M x N] out, row stride ldy >= N; 16-byte aligned, ldy % 8 == 0.
+ *          y must not overlap x.
+ * Sizes    M >= 0 (M == 0 or N == 0: nothing to do, W4V_OK), K > 0,
+ *          N % 8 == 0, K % group_size == 0; group_size must be 128
+ *          (W4V_ERR_UNSUPPORTED otherwise).
+ * alpha    epilogue scale applied to the fp32 accumulator before the single
+ *          round-to-nearest-even to fp16.
+ * workspace  device memory of at least w4a16_gemm_workspace_size(M, N, K,
+ *          group_size) bytes (may be NULL when that size is 0), 256-byte
+ *          aligned, zeroed once by the caller.  Holds fp32 split-K partial
+ *          sums and arrival counters; the result does not depend on the
+ *          order in which partial sums arrive.
+ * ---------------------------------------------------------------------- */
+size_t w4a16_gemm_workspace_size(int M, int N, int K, int group_size);
+
+int w4a16_gemm(const void* x, int64_t ldx,
+               const int32_t* qweight, const void* scales, const int32_t* qzeros,
+               void* y, int64_t ldy,
+               int M, int N, int K, int group_size, float alpha,
+               void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * 8-bit lm_head with fused greedy argmax (section 3: untied lm_head
+ * quantised to 8 bits, temperature-0 serving; section 5: W8A16 lm_head)
+ *
+ *   logit[m, v]   = float(s8[v]) * sum_h h[m, h] * q8[v, h]     (fp32, never stored)
+ *   target_ids[m] = the lowest v with the largest logit[m, v]
+ *
+ * h          fp16 [M x H], row stride ldh >= H; 16-byte aligned, ldh % 8 == 0.
+ * w          int8 [V x H] row-major, one vocabulary row per output; 16-byte
+ *            aligned.  Symmetric: no zero-point.  Any int8 value is accepted.
+ * scales     fp16 [V], one scale per vocabulary row.
+ * target_ids int32 [M] out.
+ * max_logits fp32 [M] out (the winning logit), or NULL.
+ * Sizes      M >= 0 (0: nothing to do), V > 0, H > 0 and H % 128 == 0.
+ * workspace  at least w8a16_lmhead_argmax_workspace_size(M, H, V) bytes,
+ *            256-byte aligned, zeroed once.  Holds per-block (value, index)
+ *            partials and an arrival counter.
+ * ---------------------------------------------------------------------- */
+size_t w8a16_lmhead_argmax_workspace_size(int M, int H, int V);
+
+int w8a16_lmhead_argmax(const void* h, int64_t ldh,
+                        const int8_t* w, const void* scales,
+                        int32_t* target_ids, float* max_logits,
+                        int M, int H, int V,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Greedy prefix acceptance (section 3)
+ *
+ * For each sequence b (rows b*(K+1) + j of target_ids, j = 0..K, row j being
+ * the target's greedy token after drafts 0..j-1):
+ *   accepted_len[b] = the number of leading drafts equal to their target
+ *                     token; the scan stops at the first mismatch.  A draft
+ *                     outside [0, V) -- the -1 sentinel included -- never
+ *                     matches (not an error).
+ *   out_tokens[b]   = target_ids[b][0 .. a_b] (the accepted drafts and the
+ *                     target's bonus token), then -1 up to K+1 entries.
+ *
+ * target_ids   int32 [B x (K+1)], values in [0, V).
+ * draft_ids    int32 [B x K] (may be NULL when K == 0).
+ * accepted_len int32 [B] out;  out_tokens int32 [B x (K+1)] out.
+ * Sizes        B >= 0 (0: nothing to do), K >= 0, V > 0.
+ * ---------------------------------------------------------------------- */
+int greedy_verify(const int32_t* target_ids, const int32_t* draft_ids,
+                  int B, int K, int V,
+                  int32_t* accepted_len, int32_t* out_tokens, void* stream);
+
+/* ------------------------------------------------------------------------
+ * lm_head + argmax + greedy acceptance in one launch: the block that reduces
+ * the last argmax partials also runs the prefix scan, so the verify step's
+ * tail needs no extra kernel.  Same arguments and results as
+ * w8a16_lmhead_argmax followed by greedy_verify with M = B * (K + 1);
+ * the same workspace size as w8a16_lmhead_argmax.
+ * ---------------------------------------------------------------------- */
+int w8a16_lmhead_argmax_verify(const void* h, int64_t ldh,
+                               const int8_t* w, const void* scales,
+                               int32_t* target_ids, float* max_logits,
+                               int H, int V,
+                               const int32_t* draft_ids, int B, int K,
+                               int32_t* accepted_len, int32_t* out_tokens,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* W4V_H */

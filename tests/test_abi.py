@@ -1,0 +1,163 @@
+"""The C ABI on the CPU: the library loads, exports every declared symbol,
+and rejects invalid arguments with the documented status before touching
+the device (no call here reaches a kernel launch)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import w4a16_speculative_verify_amd as w4v
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "w4v.h")
+
+OK, INVALID, UNSUPPORTED, ALIGN, WORKSPACE = 0, -1, -2, -3, -4
+A = 0x10000          # a 256-byte aligned fake device address (never dereferenced)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return re.findall(r"^\s*(?:const\s+char\s*\*|size_t|int)\s+(\w+)\s*\(", text, flags=re.M)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(w4v.LIB_PATH):
+        from w4a16_speculative_verify_amd import _build
+        _build.build()
+    return w4v.load()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert set(names) == set(w4v.SIGNATURES), "binding and header disagree"
+    out = subprocess.run(["nm", "-D", "--defined-only", w4v.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {l.split()[-1] for l in out.splitlines() if " T " in l}
+    for n in names:
+        assert n in exported, n
+        assert getattr(lib, n) is not None
+
+
+def test_version_and_status_strings(lib):
+    assert w4v.abi_version() == 1
+    for st in (OK, INVALID, UNSUPPORTED, ALIGN, WORKSPACE, -5):
+        assert w4v.status_string(st)
+    assert w4v.status_string(123) == "unknown status"
+
+
+def gemm(lib, x=A, ldx=2560, qw=A, sc=A, qz=A, y=A * 64, ldy=2560, M=16, N=2560, K=2560, g=128,
+         ws=None, wsb=0):
+    return lib.w4a16_gemm(x, ldx, qw, sc, qz, y, ldy, M, N, K, g, ctypes.c_float(1.0), ws, wsb, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(g=64), UNSUPPORTED),
+    (dict(g=0), INVALID),
+    (dict(K=100, ldx=128), INVALID),
+    (dict(K=0), INVALID),
+    (dict(N=12, ldy=16), INVALID),
+    (dict(M=-1), INVALID),
+    (dict(x=None), INVALID),
+    (dict(qz=None), INVALID),
+    (dict(ldx=2000), INVALID),
+    (dict(ldy=2000), INVALID),
+    (dict(x=A + 2), ALIGN),
+    (dict(ldx=2564), ALIGN),
+    (dict(qw=A + 4), ALIGN),
+    (dict(y=A * 64 + 8), ALIGN),
+    (dict(qz=A + 2), ALIGN),
+    (dict(y=A + 256), INVALID),                   # y overlaps x
+    (dict(M=0), OK),                              # nothing to do: no launch
+    (dict(N=0, ldy=0), OK),
+])
+def test_gemm_validation(lib, kw, status):
+    assert gemm(lib, **kw) == status
+
+
+def test_gemm_workspace(lib):
+    need = w4v.gemm_workspace_size(16, 2560, 4096)
+    assert need > 0                                # O projection splits K
+    assert gemm(lib, K=4096, ldx=4096, ws=None, wsb=0) == WORKSPACE
+    assert gemm(lib, K=4096, ldx=4096, ws=A * 256, wsb=need - 1) == WORKSPACE
+    assert gemm(lib, K=4096, ldx=4096, ws=A * 256 + 16, wsb=need) == ALIGN
+    assert w4v.gemm_workspace_size(0, 2560, 4096) == 0
+    assert w4v.gemm_workspace_size(16, 2560, 4096, 64) == 0
+    # sizes are a function of the shape alone
+    assert w4v.gemm_workspace_size(16, 2560, 4096) == need
+
+
+def lm(lib, h=A, ldh=2560, w=A, sc=A, t=A, ml=None, M=16, H=2560, V=4096, ws=A * 256, wsb=1 << 30):
+    return lib.w8a16_lmhead_argmax(h, ldh, w, sc, t, ml, M, H, V, ws, wsb, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(H=100, ldh=128), INVALID),
+    (dict(H=64, ldh=64), INVALID),
+    (dict(V=0), INVALID),
+    (dict(M=-3), INVALID),
+    (dict(h=None), INVALID),
+    (dict(t=None), INVALID),
+    (dict(ldh=1000), INVALID),
+    (dict(h=A + 8), ALIGN),
+    (dict(w=A + 1), ALIGN),
+    (dict(ml=A + 2), ALIGN),
+    (dict(ws=None, wsb=0), WORKSPACE),
+    (dict(wsb=16), WORKSPACE),
+    (dict(M=0), OK),
+])
+def test_lmhead_validation(lib, kw, status):
+    assert lm(lib, **kw) == status
+
+
+def test_lmhead_workspace_sizes(lib):
+    assert w4v.lmhead_workspace_size(16, 2560, 151936) > 0
+    assert w4v.lmhead_workspace_size(168, 2560, 151936) > w4v.lmhead_workspace_size(16, 2560, 151936)
+    assert w4v.lmhead_workspace_size(16, 100, 151936) == 0
+
+
+def gv(lib, t=A, d=A, B=2, K=15, V=4096, acc=A, out=A):
+    return lib.greedy_verify(t, d, B, K, V, acc, out, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=-1), INVALID),
+    (dict(K=-1), INVALID),
+    (dict(V=0), INVALID),
+    (dict(t=None), INVALID),
+    (dict(d=None), INVALID),
+    (dict(acc=None), INVALID),
+    (dict(out=None), INVALID),
+    (dict(t=A + 2), ALIGN),
+    (dict(B=1 << 30, K=100), INVALID),
+    (dict(B=0), OK),
+])
+def test_verify_validation(lib, kw, status):
+    assert gv(lib, **kw) == status
+
+
+def test_fused_validation(lib):
+    f = lib.w8a16_lmhead_argmax_verify
+    ws = A * 256
+    assert f(A, 2560, A, A, A, None, 2560, 4096, A, -1, 15, A, A, ws, 1 << 30, None) == INVALID
+    assert f(A, 2560, A, A, A, None, 2560, 4096, None, 1, 15, A, A, ws, 1 << 30, None) == INVALID
+    assert f(A, 2560, A, A, A, None, 2560, 4096, A, 1, 15, None, A, ws, 1 << 30, None) == INVALID
+    assert f(A, 2560, A, A, A, None, 2560, 4096, A, 1 << 28, 100, A, A, ws, 1 << 30, None) == INVALID
+    assert f(A, 2560, A, A, A, None, 100, 4096, A, 1, 15, A, A, ws, 1 << 30, None) == INVALID
+    assert f(A, 2560, A, A, A, None, 2560, 4096, A, 1, 15, A, A, None, 0, None) == WORKSPACE
+    assert f(A, 2560, A, A, A, None, 2560, 4096, A, 0, 15, A, A, None, 0, None) == OK
+
+
+def test_binding_refuses_missing_library(tmp_path):
+    import importlib
+    mod = importlib.import_module("w4a16_speculative_verify_amd")
+    saved = mod._lib
+    try:
+        mod._lib = None
+        with pytest.raises(RuntimeError, match="no fallback"):
+            mod.load(str(tmp_path / "missing.so"))
+    finally:
+        mod._lib = saved

@@ -1,0 +1,163 @@
+"""GPU parity of the W4A16 linear against the fp64 oracle (G1), plus exact
+cases (identity / one-hot weights), strides, determinism and workspace reuse."""
+import numpy as np
+import pytest
+
+import gen
+from oracle import gemm as og
+from tests.gpu_util import check_gemm, dev, host, log
+
+pytestmark = pytest.mark.gpu
+
+
+def run_gemm(w4v, x, lin, alpha=1.0, ws=None):
+    y = w4v.w4a16_gemm(dev(x), dev(lin.qweight), dev(lin.scales), dev(lin.qzeros), alpha=alpha,
+                       workspace=ws)
+    import torch
+    torch.cuda.synchronize()
+    return host(y)
+
+
+@pytest.mark.parametrize("m,k,n", [
+    (16, 2560, 2560),          # block linear at M = 16
+    (1, 2560, 2560),
+    (5, 384, 200),             # ragged N (not a multiple of 64)
+    (16, 1280, 72),
+    (21, 1280, 520),           # M = K+1 with K = 20: two m-tiles, ragged rows
+    (32, 128, 8),              # single group, narrowest N
+    (40, 640, 136),            # more than one m-block
+    (16, 9728, 2560),          # deep K (split across blocks)
+    (16, 4096, 2560),
+    (3, 9728, 1032),
+])
+def test_random_shapes(lib, m, k, n):
+    log(f"gemm m={m} k={k} n={n}")
+    rng = np.random.default_rng(1000 + m * 7 + k + n)
+    lin = gen.qlinear(rng, k, n)
+    x = gen.activations(rng, m, k)
+    y = run_gemm(lib, x, lin)
+    rel, mx = check_gemm(y, og.w4a16_gemm(x, lin.qweight, lin.scales, lin.qzeros), f"{m}x{k}x{n}")
+    log(f"  rel-L2 {rel:.2e} max/rms {mx:.2e}")
+
+
+@pytest.mark.parametrize("enc", range(3))
+@pytest.mark.parametrize("m", [16, 21])
+def test_identity_weights_bit_exact(lib, enc, m):
+    n = 512
+    eye = np.eye(n, dtype=np.int64)
+    g = n // 128
+    q, z, s = [
+        (eye, np.zeros((g, n), np.int64), np.ones((g, n), np.float16)),
+        (8 + eye, np.full((g, n), 8, np.int64), np.ones((g, n), np.float16)),
+        (7 + 2 * eye, np.full((g, n), 7, np.int64), np.full((g, n), 0.5, np.float16)),
+    ][enc]
+    lin = gen.QLinear(gen.pack_int4_along_k(q), s, gen.pack_int4_along_n(z), n, n)
+    x = gen.activations(np.random.default_rng(enc), m, n)
+    y = run_gemm(lib, x, lin)
+    assert np.array_equal(y.view(np.uint16), x.view(np.uint16))
+
+
+def test_one_hot_weight(lib):
+    k, n, m = 1024, 264, 16
+    k0, n0 = 517, 203
+    q = np.full((k, n), 5, dtype=np.int64)
+    z = np.full((k // 128, n), 5, dtype=np.int64)
+    q[k0, n0] = 13                                   # q - z = 8, scale 0.125 -> w = 1
+    s = np.full((k // 128, n), 0.125, dtype=np.float16)
+    lin = gen.QLinear(gen.pack_int4_along_k(q), s, gen.pack_int4_along_n(z), k, n)
+    x = gen.activations(np.random.default_rng(9), m, k)
+    y = run_gemm(lib, x, lin)
+    expect = np.zeros((m, n), dtype=np.float16)
+    expect[:, n0] = x[:, k0]
+    assert np.array_equal(y.view(np.uint16), expect.view(np.uint16))
+
+
+def test_extreme_codes_and_alpha(lib):
+    # q - z at +-15 everywhere with alternating signs, alpha != 1
+    k, n, m = 768, 128, 16
+    rng = np.random.default_rng(4)
+    q = np.where(rng.random((k, n)) < 0.5, 0, 15)
+    z = np.where(rng.random((k // 128, n)) < 0.5, 0, 15)
+    s = gen.group_scales(rng, k // 128, n)
+    lin = gen.QLinear(gen.pack_int4_along_k(q), s, gen.pack_int4_along_n(z), k, n)
+    x = gen.activations(rng, m, k)
+    y = run_gemm(lib, x, lin, alpha=0.37)
+    check_gemm(y, og.w4a16_gemm(x, lin.qweight, lin.scales, lin.qzeros, alpha=0.37), "extreme")
+
+
+def test_strided_input_and_output(lib):
+    import torch
+    rng = np.random.default_rng(12)
+    k, n, m = 4096, 2560, 16
+    lin = gen.qlinear(rng, k, n)
+    wide = gen.activations(rng, m, 6144)               # O reads 4096 of QKV's 6144 columns
+    out_wide = torch.full((m, 3000), 7.0, dtype=torch.float16, device="cuda")
+    out = out_wide[:, 200:200 + n]
+    lib.w4a16_gemm(dev(wide)[:, :k], dev(lin.qweight), dev(lin.scales), dev(lin.qzeros), out=out)
+    torch.cuda.synchronize()
+    full = host(out_wide)
+    check_gemm(full[:, 200:200 + n], og.w4a16_gemm(wide[:, :k], lin.qweight, lin.scales, lin.qzeros),
+               "strided")
+    assert np.all(full[:, :200] == 7.0) and np.all(full[:, 200 + n:] == 7.0)
+
+
+@pytest.mark.parametrize("k,n", [(9728, 2560), (4096, 2560), (2560, 6144)])
+def test_deterministic_and_workspace_reuse(lib, k, n):
+    rng = np.random.default_rng(k + n)
+    lin = gen.qlinear(rng, k, n)
+    x1 = gen.activations(rng, 16, k)
+    x2 = gen.activations(rng, 16, k)
+    need = lib.gemm_workspace_size(16, n, k)
+    ws = lib.new_workspace(need) if need else None
+    a = run_gemm(lib, x1, lin, ws=ws)
+    b = run_gemm(lib, x2, lin, ws=ws)           # counters re-armed by the kernel
+    c = run_gemm(lib, x1, lin, ws=ws)
+    assert np.array_equal(a.view(np.uint16), c.view(np.uint16))
+    check_gemm(b, og.w4a16_gemm(x2, lin.qweight, lin.scales, lin.qzeros), "reuse")
+    if ws is not None:
+        import torch
+        assert int(torch.count_nonzero(ws[:65536])) == 0     # counters back at zero
+
+
+def test_workspace_shared_across_shapes(lib):
+    """One workspace for linears of different shapes, in chain order (as a verify step does)."""
+    rng = np.random.default_rng(21)
+    shapes = [(2560, 6144), (4096, 2560), (2560, 19456), (9728, 2560), (2560, 6144)]
+    lins = [gen.qlinear(rng, k, n) for k, n in shapes]
+    need = max(lib.gemm_workspace_size(16, n, k) for k, n in shapes)
+    ws = lib.new_workspace(need)
+    for rep in range(2):
+        for lin, (k, n) in zip(lins, shapes):
+            x = gen.activations(rng, 16, k)
+            y = run_gemm(lib, x, lin, ws=ws)
+            check_gemm(y, og.w4a16_gemm(x, lin.qweight, lin.scales, lin.qzeros), f"{k}->{n}")
+
+
+@pytest.mark.parametrize("lin_idx", range(4))
+def test_layer_linears_m16(lib, lin_idx):
+    """The four linears of the 4B-class layer at the verify block size M = 16."""
+    wl = gen.make_workload(3, layers=1, vocab=0)
+    k_in, n_out, alpha = gen.chain_plan(wl.cfg)[lin_idx]
+    lin = wl.linears[lin_idx]
+    x = gen.activations(np.random.default_rng(77 + lin_idx), 16, k_in)
+    log(f"layer linear {lin_idx}: {k_in}->{n_out}")
+    y = run_gemm(lib, x, lin, alpha=alpha)
+    check_gemm(y, og.w4a16_gemm(x, lin.qweight, lin.scales, lin.qzeros, alpha=alpha), "layer")
+
+
+@pytest.mark.parametrize("m", [168, 2048, 8192])
+@pytest.mark.parametrize("shape", [(2560, 19456), (9728, 2560)])
+def test_large_m_sampled_columns(lib, m, shape):
+    """Verify-batch (M = 168) and prefill (M = 2048, 8192) shapes: every row, sampled columns."""
+    k, n = shape
+    wl = gen.make_workload(5, m=m)
+    lin = wl.linears[0] if k == 2560 else wl.linears[1]
+    x = wl.extra_x[0] if k == 2560 else wl.extra_x[1]
+    log(f"large-m m={m} {k}->{n}")
+    y = run_gemm(lib, x, lin)
+    rng = np.random.default_rng(m + k)
+    cols = np.sort(rng.choice(n, 96, replace=False))
+    cols[0], cols[-1] = 0, n - 1
+    ref = og.w4a16_gemm_columns(x, lin.qweight, lin.scales, lin.qzeros, cols)
+    check_gemm(y[:, cols], ref, f"m={m} {k}->{n}")
+    assert np.all(np.isfinite(y.astype(np.float32)))

@@ -1,0 +1,239 @@
+"""Python binding of libw4v (W4A16 speculative-verify kernels for gfx950).
+
+Argument marshalling only: every step of the path runs in the HIP library.
+PyTorch supplies device memory and the current stream.  The binding raises
+``W4VError`` on a non-zero status and ``RuntimeError`` when the library has
+not been built -- there is no fallback implementation.
+
+The calls follow the organisers' page "Efficient LLM Challenge Results",
+section 3 (W4A16 group-128 target, 8-bit lm_head, greedy verification of K
+drafts padded with -1 sentinels); the C declarations are in include/w4v.h.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libw4v.so")
+
+_lib = None
+
+W4V_OK = 0
+W4V_ERR_INVALID_ARG = -1
+W4V_ERR_UNSUPPORTED = -2
+W4V_ERR_ALIGNMENT = -3
+W4V_ERR_WORKSPACE = -4
+W4V_ERR_HIP = -5
+
+GROUP_SIZE = 128
+
+_vp = ctypes.c_void_p
+_i64 = ctypes.c_int64
+_int = ctypes.c_int
+_sz = ctypes.c_size_t
+
+# name -> (restype, argtypes); mirrors include/w4v.h
+SIGNATURES = {
+    "w4v_status_string": (ctypes.c_char_p, [_int]),
+    "w4v_abi_version": (_int, []),
+    "w4a16_gemm_workspace_size": (_sz, [_int, _int, _int, _int]),
+    "w4a16_gemm": (_int, [_vp, _i64, _vp, _vp, _vp, _vp, _i64, _int, _int, _int, _int,
+                          ctypes.c_float, _vp, _sz, _vp]),
+    "w8a16_lmhead_argmax_workspace_size": (_sz, [_int, _int, _int]),
+    "w8a16_lmhead_argmax": (_int, [_vp, _i64, _vp, _vp, _vp, _vp, _int, _int, _int, _vp, _sz,
+                                   _vp]),
+    "greedy_verify": (_int, [_vp, _vp, _int, _int, _int, _vp, _vp, _vp]),
+    "w8a16_lmhead_argmax_verify": (_int, [_vp, _i64, _vp, _vp, _vp, _vp, _int, _int, _vp, _int,
+                                          _int, _vp, _vp, _vp, _sz, _vp]),
+}
+
+
+class W4VError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)} (status {status})")
+
+
+def load(path: str | None = None):
+    """Load libw4v.so (once).  Raises RuntimeError if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = path or LIB_PATH
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with __graft_entry__.build() "
+                           "(hipcc, gfx950); there is no fallback path")
+    lib = ctypes.CDLL(path)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load().w4v_status_string(status).decode()
+
+
+def abi_version() -> int:
+    return load().w4v_abi_version()
+
+
+def _check(status: int, where: str):
+    if status != W4V_OK:
+        raise W4VError(status, where)
+
+
+def _stream(stream=None):
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def _require(t, dtype, name):
+    import torch
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.dim() >= 1 and t.numel() > 0 and t.stride(-1) != 1:
+        raise ValueError(f"{name} must have unit stride in its last dimension")
+    return torch
+
+
+# ------------------------------------------------------------------- workspaces
+def gemm_workspace_size(m: int, n: int, k: int, group_size: int = GROUP_SIZE) -> int:
+    return int(load().w4a16_gemm_workspace_size(m, n, k, group_size))
+
+
+def lmhead_workspace_size(m: int, h: int, v: int) -> int:
+    return int(load().w8a16_lmhead_argmax_workspace_size(m, h, v))
+
+
+def new_workspace(nbytes: int, device="cuda"):
+    """Zeroed device workspace (uint8) of at least ``nbytes`` bytes, 256-byte aligned."""
+    import torch
+    t = torch.zeros(max(int(nbytes), 1) + 256, dtype=torch.uint8, device=device)
+    off = (-t.data_ptr()) % 256
+    return t[off:off + max(int(nbytes), 1)]
+
+
+# ------------------------------------------------------------------- calls
+def w4a16_gemm(x, qweight, scales, qzeros, alpha: float = 1.0, out=None, workspace=None,
+               group_size: int = GROUP_SIZE, stream=None):
+    """y[M, N] = fp16(alpha * x[:, :K] @ dequant(qweight, scales, qzeros)).
+
+    x: fp16 [M, >=K] (a column slice of a wider tensor is fine: its row stride
+    is passed as ldx); qweight: int32 [K/8, N]; scales: fp16 [K/128, N];
+    qzeros: int32 [K/128, N/8].  ``out`` may be a row-strided fp16 [M, N] view.
+    """
+    torch = _require(x, __import__("torch").float16, "x")
+    _require(qweight, torch.int32, "qweight")
+    _require(scales, torch.float16, "scales")
+    _require(qzeros, torch.int32, "qzeros")
+    k = qweight.shape[0] * 8
+    n = qweight.shape[1]
+    m = x.shape[0]
+    if x.shape[1] < k:
+        raise ValueError(f"x has {x.shape[1]} columns, the weights need {k}")
+    if out is None:
+        out = torch.empty((m, n), dtype=torch.float16, device=x.device)
+    _require(out, torch.float16, "out")
+    need = gemm_workspace_size(m, n, k, group_size)
+    if workspace is None and need > 0:
+        workspace = new_workspace(need, x.device)
+    wbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = load().w4a16_gemm(_ptr(x), x.stride(0), _ptr(qweight), _ptr(scales), _ptr(qzeros),
+                           _ptr(out), out.stride(0), m, n, k, group_size, ctypes.c_float(alpha),
+                           _ptr(workspace), wbytes, _stream(stream))
+    _check(st, "w4a16_gemm")
+    return out
+
+
+def w8a16_lmhead_argmax(h, w, scales, target_ids=None, max_logits=None, want_max=True,
+                        workspace=None, stream=None):
+    """(target_ids int32 [M], max_logits fp32 [M] or None) for h fp16 [M, H], w int8 [V, H]."""
+    torch = _require(h, __import__("torch").float16, "h")
+    _require(w, torch.int8, "w")
+    _require(scales, torch.float16, "scales")
+    m, hdim = h.shape[0], w.shape[1]
+    v = w.shape[0]
+    if target_ids is None:
+        target_ids = torch.empty(m, dtype=torch.int32, device=h.device)
+    if want_max and max_logits is None:
+        max_logits = torch.empty(m, dtype=torch.float32, device=h.device)
+    need = lmhead_workspace_size(m, hdim, v)
+    if workspace is None and need > 0:
+        workspace = new_workspace(need, h.device)
+    wbytes = workspace.numel() if workspace is not None else 0
+    st = load().w8a16_lmhead_argmax(_ptr(h), h.stride(0), _ptr(w), _ptr(scales),
+                                    _ptr(target_ids), _ptr(max_logits), m, hdim, v,
+                                    _ptr(workspace), wbytes, _stream(stream))
+    _check(st, "w8a16_lmhead_argmax")
+    return target_ids, max_logits
+
+
+def greedy_verify(target_ids, draft_ids, vocab: int, accepted_len=None, out_tokens=None,
+                  stream=None):
+    """(accepted_len int32 [B], out_tokens int32 [B, K+1]) from target_ids [B, K+1], drafts [B, K]."""
+    torch = _require(target_ids, __import__("torch").int32, "target_ids")
+    b, k1 = target_ids.shape
+    k = k1 - 1
+    _require(draft_ids, torch.int32, "draft_ids")
+    if tuple(draft_ids.shape) != (b, k):
+        raise ValueError(f"draft_ids must be [{b}, {k}], got {tuple(draft_ids.shape)}")
+    if not (target_ids.is_contiguous() and draft_ids.is_contiguous()):
+        raise ValueError("target_ids and draft_ids must be contiguous")
+    if accepted_len is None:
+        accepted_len = torch.empty(b, dtype=torch.int32, device=target_ids.device)
+    if out_tokens is None:
+        out_tokens = torch.empty((b, k1), dtype=torch.int32, device=target_ids.device)
+    st = load().greedy_verify(_ptr(target_ids), _ptr(draft_ids) if k > 0 else None, b, k, vocab,
+                              _ptr(accepted_len), _ptr(out_tokens), _stream(stream))
+    _check(st, "greedy_verify")
+    return accepted_len, out_tokens
+
+
+def w8a16_lmhead_argmax_verify(h, w, scales, draft_ids, target_ids=None, max_logits=None,
+                               accepted_len=None, out_tokens=None, want_max=True,
+                               workspace=None, stream=None):
+    """lm_head + argmax + greedy verify in one launch; h has B*(K+1) rows.
+
+    Returns (target_ids [B*(K+1)], max_logits or None, accepted_len [B], out_tokens [B, K+1]).
+    """
+    torch = _require(h, __import__("torch").float16, "h")
+    _require(w, torch.int8, "w")
+    _require(scales, torch.float16, "scales")
+    _require(draft_ids, torch.int32, "draft_ids")
+    b, k = draft_ids.shape
+    m = b * (k + 1)
+    if h.shape[0] != m:
+        raise ValueError(f"h has {h.shape[0]} rows, B*(K+1) = {m}")
+    if not draft_ids.is_contiguous():
+        raise ValueError("draft_ids must be contiguous")
+    hdim, v = w.shape[1], w.shape[0]
+    dev = h.device
+    if target_ids is None:
+        target_ids = torch.empty(m, dtype=torch.int32, device=dev)
+    if want_max and max_logits is None:
+        max_logits = torch.empty(m, dtype=torch.float32, device=dev)
+    if accepted_len is None:
+        accepted_len = torch.empty(b, dtype=torch.int32, device=dev)
+    if out_tokens is None:
+        out_tokens = torch.empty((b, k + 1), dtype=torch.int32, device=dev)
+    need = lmhead_workspace_size(m, hdim, v)
+    if workspace is None and need > 0:
+        workspace = new_workspace(need, dev)
+    wbytes = workspace.numel() if workspace is not None else 0
+    st = load().w8a16_lmhead_argmax_verify(
+        _ptr(h), h.stride(0), _ptr(w), _ptr(scales), _ptr(target_ids), _ptr(max_logits), hdim, v,
+        _ptr(draft_ids) if k > 0 else None, b, k, _ptr(accepted_len), _ptr(out_tokens),
+        _ptr(workspace), wbytes, _stream(stream))
+    _check(st, "w8a16_lmhead_argmax_verify")
+    return target_ids, max_logits, accepted_len, out_tokens

@@ -1,0 +1,78 @@
+// Host-side launch plans and launchers of libw4v (internal header).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace w4v {
+
+constexpr int kGroup = 128;        // quantisation group along k
+constexpr int kColTile = 64;       // output columns per wave (4 per lane x 16 lanes)
+constexpr int kWorkspaceAlign = 256;
+
+// Every workspace that needs arrival counters starts with this fixed counter
+// region (one 32-bit counter per output tile); partial results follow it.
+// Because the counters sit at the same place for every shape and every
+// kernel leaves them at zero, calls of different shapes may share one
+// workspace as long as they are ordered on one stream.
+constexpr size_t kTicketRegion = 64 * 1024;
+constexpr size_t kMaxTickets = kTicketRegion / sizeof(unsigned);
+
+inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+// ---------------------------------------------------------------- W4A16 GEMM
+struct GemmArgs {
+  const _Float16* x; int64_t ldx;
+  const uint32_t* qweight; const _Float16* scales; const uint32_t* qzeros;
+  _Float16* y; int64_t ldy;
+  int M, N, K;
+  float alpha;
+};
+
+struct GemmPlan {
+  int mt;            // 16-row m-tiles per block (1 or 2)
+  int mblocks;       // blocks along M, each 16*mt rows
+  int col_tiles;     // ceil(N / 64)
+  int splits;        // split-K factor across blocks (1 = none)
+  int gw;            // groups a wave loads before computing (1..4)
+  size_t ticket_bytes;
+  size_t partial_bytes;
+  size_t workspace_bytes() const { return ticket_bytes + partial_bytes; }
+};
+
+GemmPlan plan_w4a16(int M, int N, int K, int num_cus);
+hipError_t launch_w4a16_skinny(const GemmArgs& a, const GemmPlan& p, void* workspace,
+                               hipStream_t stream);
+
+// ---------------------------------------------------------------- lm_head
+struct LmheadArgs {
+  const _Float16* h; int64_t ldh;
+  const int8_t* w; const _Float16* scales;
+  int32_t* target_ids; float* max_logits;
+  int M, H, V;
+  // fused greedy verify (draft_ids may be NULL when K == 0; B == 0 disables it)
+  const int32_t* draft_ids; int B, K;
+  int32_t* accepted_len; int32_t* out_tokens;
+};
+
+struct LmheadPlan {
+  int mt;            // 16-row m-tiles per block (1 or 2)
+  int mblocks;
+  int tiles;         // 16-row vocabulary tiles per wave pass (1 or 4)
+  int vblocks;       // blocks along the vocabulary
+  size_t ticket_bytes;
+  size_t partial_bytes;
+  size_t workspace_bytes() const { return ticket_bytes + partial_bytes; }
+};
+
+LmheadPlan plan_lmhead(int M, int H, int V, int num_cus);
+hipError_t launch_lmhead_argmax(const LmheadArgs& a, const LmheadPlan& p, void* workspace,
+                                hipStream_t stream);
+
+// ---------------------------------------------------------------- verify
+hipError_t launch_greedy_verify(const int32_t* target_ids, const int32_t* draft_ids, int B, int K,
+                                int V, int32_t* accepted_len, int32_t* out_tokens,
+                                hipStream_t stream);
+
+}  // namespace w4v
