@@ -77,6 +77,8 @@ def main():
                     help="replays of the linears-only graph for the roofline timing")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--path", choices=["chain", "per-linear"], default="per-linear",
+                    help="one persistent launch for all linears, or one launch per linear")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -105,7 +107,8 @@ def main():
 
     lins = [DeviceLinear(up(l.qweight), up(l.scales), up(l.qzeros), k, n, a)
             for l, (k, n, a) in zip(wl.linears, plan)]
-    step = VerifyStep(lins, up(wl.lm_w), up(wl.lm_s), cfg.m, cfg.batch, cfg.k_draft)
+    step = VerifyStep(lins, up(wl.lm_w), up(wl.lm_s), cfg.m, cfg.batch, cfg.k_draft,
+                      chain=args.path == "chain")
     x = up(wl.x)
     torch.cuda.synchronize()
 

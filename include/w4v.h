@@ -149,6 +149,56 @@ int w8a16_lmhead_argmax_verify(const void* h, int64_t ldh,
                                int32_t* accepted_len, int32_t* out_tokens,
                                void* workspace, size_t workspace_bytes, void* stream);
 
+/* ------------------------------------------------------------------------
+ * A chain of W4A16 linears in one launch (section 3: the target's forward
+ * pass over the verify block -- every linear of every layer -- at M <= 16
+ * rows).  Linear l reads the leading K_l columns of linear l-1's output
+ * (K_l <= N_{l-1}); the first reads x, the last writes y:
+ *
+ *   h_0 = x;  h_l = fp16_rne( alpha_l * h_{l-1}[:, :K_l] @ W_l ),  y = h_{n-1}
+ *
+ * with W_l in the layout of w4a16_gemm.  Each intermediate output is rounded
+ * to fp16 exactly as a separate w4a16_gemm call would round it.
+ *
+ * w4a16_chain_prepare writes the launch plan (unit tables, per-linear
+ * buffers, counters) into the caller's workspace with synchronous copies; it
+ * must not run while a call that uses this workspace is in flight.  The
+ * prepared workspace is then used by any number of w4a16_chain calls ordered
+ * on one stream (also from a captured graph: the kernel re-arms its own
+ * counters).  The linears' device arrays must stay valid and unchanged.
+ *
+ * linears    host array of n_linears descriptors (device pointers inside),
+ *            1 <= n_linears <= 65535; K % 128 == 0, N % 8 == 0, qweight and
+ *            scales 16-byte aligned, qzeros 4-byte aligned.
+ * M          1..16 rows (W4V_ERR_UNSUPPORTED above 16).
+ * x          fp16 [M x K_0], row stride ldx >= K_0, 16-byte aligned, ldx % 8 == 0.
+ * y          fp16 [M x N_{n-1}], row stride ldy >= N_{n-1}, 16-byte aligned,
+ *            ldy % 8 == 0; must not overlap x.
+ * workspace  w4a16_chain_workspace_size(...) bytes, 256-byte aligned.  Byte
+ *            offset 28 holds an error word the kernel sets (sticky until the
+ *            caller clears it): 1 = a dependency wait exceeded its bound
+ *            (results invalid), 2 = the workspace was not prepared for this
+ *            M, K_0 and N_{n-1} (nothing computed).
+ * The work is handed out dynamically, and each output element is computed in
+ * a fixed order, so results are bit-identical from call to call.
+ * ---------------------------------------------------------------------- */
+typedef struct {
+  const int32_t* qweight;   /* int32 [K/8 x N]   */
+  const void* scales;       /* fp16  [K/128 x N] */
+  const int32_t* qzeros;    /* int32 [K/128 x N/8] */
+  int K;
+  int N;
+  float alpha;
+} w4v_chain_linear;
+
+size_t w4a16_chain_workspace_size(const w4v_chain_linear* linears, int n_linears, int M);
+
+int w4a16_chain_prepare(const w4v_chain_linear* linears, int n_linears, int M,
+                        void* workspace, size_t workspace_bytes);
+
+int w4a16_chain(const void* x, int64_t ldx, void* y, int64_t ldy, int M, int K0, int N_last,
+                void* workspace, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

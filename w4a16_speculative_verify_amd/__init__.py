@@ -49,6 +49,22 @@ SIGNATURES = {
 }
 
 
+class ChainLinearDesc(ctypes.Structure):
+    """Mirror of w4v_chain_linear (include/w4v.h)."""
+    _fields_ = [("qweight", ctypes.c_void_p), ("scales", ctypes.c_void_p),
+                ("qzeros", ctypes.c_void_p), ("K", ctypes.c_int), ("N", ctypes.c_int),
+                ("alpha", ctypes.c_float)]
+
+
+SIGNATURES.update({
+    "w4a16_chain_workspace_size": (_sz, [_vp, _int, _int]),
+    "w4a16_chain_prepare": (_int, [_vp, _int, _int, _vp, _sz]),
+    "w4a16_chain": (_int, [_vp, _i64, _vp, _i64, _int, _int, _int, _vp, _vp]),
+})
+
+CHAIN_ERROR_OFFSET = 28      # byte offset of the chain workspace's error word
+
+
 class W4VError(RuntimeError):
     def __init__(self, status: int, where: str):
         self.status = status
@@ -237,3 +253,56 @@ def w8a16_lmhead_argmax_verify(h, w, scales, draft_ids, target_ids=None, max_log
         _ptr(workspace), wbytes, _stream(stream))
     _check(st, "w8a16_lmhead_argmax_verify")
     return target_ids, max_logits, accepted_len, out_tokens
+
+
+# ------------------------------------------------------------------- chain of linears
+class Chain:
+    """A prepared chain of W4A16 linears run in one launch (w4a16_chain).
+
+    ``linears``: sequence of (qweight, scales, qzeros, alpha) GPU tensors in
+    the w4a16_gemm layouts; linear l reads the leading K_l columns of linear
+    l-1's output.  The workspace is allocated and prepared here, once.
+    """
+
+    def __init__(self, linears, m: int, device="cuda"):
+        import torch
+        self.m = int(m)
+        self._keep = list(linears)
+        descs = (ChainLinearDesc * len(self._keep))()
+        for d, (qw, sc, qz, alpha) in zip(descs, self._keep):
+            _require(qw, torch.int32, "qweight")
+            _require(sc, torch.float16, "scales")
+            _require(qz, torch.int32, "qzeros")
+            d.qweight, d.scales, d.qzeros = qw.data_ptr(), sc.data_ptr(), qz.data_ptr()
+            d.K, d.N, d.alpha = qw.shape[0] * 8, qw.shape[1], float(alpha)
+        self._descs = descs
+        self.k0 = descs[0].K
+        self.n_last = descs[len(descs) - 1].N
+        lib = load()
+        need = int(lib.w4a16_chain_workspace_size(ctypes.cast(descs, ctypes.c_void_p),
+                                                  len(descs), self.m))
+        if need == 0:
+            # re-run the checks through prepare to get the status
+            _check(lib.w4a16_chain_prepare(ctypes.cast(descs, ctypes.c_void_p), len(descs),
+                                           self.m, None, 0), "w4a16_chain_prepare")
+        self.workspace = new_workspace(need, device)
+        _check(lib.w4a16_chain_prepare(ctypes.cast(descs, ctypes.c_void_p), len(descs), self.m,
+                                       _ptr(self.workspace), need), "w4a16_chain_prepare")
+
+    def __call__(self, x, out=None, stream=None):
+        import torch
+        _require(x, torch.float16, "x")
+        if x.shape[0] != self.m or x.shape[1] < self.k0:
+            raise ValueError(f"x must be [{self.m}, >={self.k0}]")
+        if out is None:
+            out = torch.empty((self.m, self.n_last), dtype=torch.float16, device=x.device)
+        _require(out, torch.float16, "out")
+        st = load().w4a16_chain(_ptr(x), x.stride(0), _ptr(out), out.stride(0), self.m, self.k0,
+                                self.n_last, _ptr(self.workspace), _stream(stream))
+        _check(st, "w4a16_chain")
+        return out
+
+    def error(self) -> int:
+        """The kernel's error word (synchronises): 0 ok, 1 wait timed out, 2 not prepared."""
+        w = self.workspace[CHAIN_ERROR_OFFSET:CHAIN_ERROR_OFFSET + 4]
+        return int(w.cpu().view(__import__("torch").int32).item())

@@ -4,6 +4,9 @@
 #include <hip/hip_runtime.h>
 
 #include <stdint.h>
+#include <string.h>
+
+#include <vector>
 
 #include "w4v.h"
 #include "w4v_launch.h"
@@ -86,6 +89,67 @@ int run_lmhead(const void* h, int64_t ldh, const int8_t* w, const void* scales,
   a.out_tokens = out_tokens;
   hipError_t e = w4v::launch_lmhead_argmax(a, p, workspace, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? W4V_OK : W4V_ERR_HIP;
+}
+
+int chain_splits(int K) {
+  const int G = K / w4v::kGroup;
+  const int per_unit = w4v::kChainWavesPerUnit * w4v::kChainGroupsPerWave;
+  return (G + per_unit - 1) / per_unit;
+}
+
+// Checks the descriptors and lays out the workspace.  Host-only.
+int chain_layout(const w4v_chain_linear* lins, int n, int M, w4v::ChainLayout* lay) {
+  if (!lins || n < 1 || n > 65535) return W4V_ERR_INVALID_ARG;
+  if (M < 1) return W4V_ERR_INVALID_ARG;
+  if (M > w4v::kChainMaxRows) return W4V_ERR_UNSUPPORTED;
+  size_t off = 256;
+  lay->lin_offset = off;
+  off += w4v::align_up((size_t)n * sizeof(w4v::ChainLinear), 256);
+  long long units = 0;
+  for (int l = 0; l < n; ++l) {
+    const w4v_chain_linear& L = lins[l];
+    if (L.K <= 0 || L.N <= 0 || L.K % w4v::kGroup != 0 || L.N % 8 != 0) return W4V_ERR_INVALID_ARG;
+    if (l > 0 && L.K > lins[l - 1].N) return W4V_ERR_INVALID_ARG;
+    if (!L.qweight || !L.scales || !L.qzeros) return W4V_ERR_INVALID_ARG;
+    if (!aligned(L.qweight, 16) || !aligned(L.scales, 16) || !aligned(L.qzeros, 4))
+      return W4V_ERR_ALIGNMENT;
+    const int ct = (L.N + w4v::kColTile - 1) / w4v::kColTile;
+    units += (long long)ct * chain_splits(L.K);
+  }
+  if (units >= (1LL << 31)) return W4V_ERR_UNSUPPORTED;
+  lay->total_units = (unsigned)units;
+  lay->unit_offset = off;
+  off += w4v::align_up((size_t)units * sizeof(uint16_t), 256);
+  lay->counters_offset = off;
+  size_t cnt = 0;
+  for (int l = 0; l < n; ++l) {
+    const int ct = (lins[l].N + w4v::kColTile - 1) / w4v::kColTile;
+    cnt += w4v::align_up((size_t)2 * ct * sizeof(unsigned), 256);
+  }
+  lay->counters_bytes = cnt;
+  off += cnt;
+  for (int l = 0; l < n; ++l) {
+    const size_t ldo = (size_t)((lins[l].N + w4v::kColTile - 1) / w4v::kColTile) * w4v::kColTile;
+    if (l < n - 1) off += w4v::align_up(16 * ldo * 2, 256);
+    const int S = chain_splits(lins[l].K);
+    if (S > 1) off += w4v::align_up((size_t)S * 16 * ldo * 4, 256);
+  }
+  lay->bytes = off;
+  return W4V_OK;
+}
+
+int chain_blocks() {
+  static int cached_dev = -1, cached_cus = 0;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (dev != cached_dev) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return 0;
+    cached_cus = cus;
+    cached_dev = dev;
+  }
+  return cached_cus;
 }
 
 }  // namespace
@@ -184,6 +248,93 @@ int w8a16_lmhead_argmax_verify(const void* h, int64_t ldh, const int8_t* w, cons
     return W4V_ERR_ALIGNMENT;
   return run_lmhead(h, ldh, w, scales, target_ids, max_logits, M, H, V, draft_ids, B, K,
                     accepted_len, out_tokens, workspace, workspace_bytes, stream);
+}
+
+size_t w4a16_chain_workspace_size(const w4v_chain_linear* linears, int n_linears, int M) {
+  w4v::ChainLayout lay{};
+  if (chain_layout(linears, n_linears, M, &lay) != W4V_OK) return 0;
+  return lay.bytes;
+}
+
+int w4a16_chain_prepare(const w4v_chain_linear* linears, int n_linears, int M, void* workspace,
+                        size_t workspace_bytes) {
+  w4v::ChainLayout lay{};
+  int st = chain_layout(linears, n_linears, M, &lay);
+  if (st != W4V_OK) return st;
+  if (!workspace || workspace_bytes < lay.bytes) return W4V_ERR_WORKSPACE;
+  if (!aligned(workspace, 256)) return W4V_ERR_ALIGNMENT;
+  char* base = static_cast<char*>(workspace);
+  std::vector<char> img(lay.counters_offset, 0);
+  w4v::ChainHeader* hdr = reinterpret_cast<w4v::ChainHeader*>(img.data());
+  hdr->magic = w4v::kChainMagic;
+  hdr->n_linears = (unsigned)n_linears;
+  hdr->total_units = lay.total_units;
+  hdr->M = (unsigned)M;
+  hdr->K0 = (unsigned)linears[0].K;
+  hdr->N_last = (unsigned)linears[n_linears - 1].N;
+  hdr->lin_offset = lay.lin_offset;
+  hdr->unit_offset = lay.unit_offset;
+  w4v::ChainLinear* tab = reinterpret_cast<w4v::ChainLinear*>(img.data() + lay.lin_offset);
+  uint16_t* unit_lin = reinterpret_cast<uint16_t*>(img.data() + lay.unit_offset);
+  size_t cnt_off = lay.counters_offset;
+  size_t buf_off = lay.counters_offset + lay.counters_bytes;
+  unsigned u0 = 0;
+  for (int l = 0; l < n_linears; ++l) {
+    const w4v_chain_linear& L = linears[l];
+    w4v::ChainLinear& d = tab[l];
+    const int ct = (L.N + w4v::kColTile - 1) / w4v::kColTile;
+    const int S = chain_splits(L.K);
+    d.qweight = reinterpret_cast<const uint32_t*>(L.qweight);
+    d.scales = static_cast<const _Float16*>(L.scales);
+    d.qzeros = reinterpret_cast<const uint32_t*>(L.qzeros);
+    d.K = L.K;
+    d.N = L.N;
+    d.ct = ct;
+    d.splits = S;
+    d.unit0 = (int)u0;
+    d.alpha = L.alpha;
+    d.ldo = ct * w4v::kColTile;
+    d.flags = reinterpret_cast<unsigned*>(base + cnt_off);
+    d.tickets = reinterpret_cast<unsigned*>(base + cnt_off + (size_t)ct * sizeof(unsigned));
+    cnt_off += w4v::align_up((size_t)2 * ct * sizeof(unsigned), 256);
+    d.out = nullptr;
+    if (l < n_linears - 1) {
+      d.out = reinterpret_cast<_Float16*>(base + buf_off);
+      buf_off += w4v::align_up(16 * (size_t)d.ldo * 2, 256);
+    }
+    d.partials = nullptr;
+    if (S > 1) {
+      d.partials = reinterpret_cast<float*>(base + buf_off);
+      buf_off += w4v::align_up((size_t)S * 16 * d.ldo * 4, 256);
+    }
+    for (int u = 0; u < ct * S; ++u) unit_lin[u0 + u] = (uint16_t)l;
+    u0 += (unsigned)(ct * S);
+  }
+  if (hipMemcpy(workspace, img.data(), img.size(), hipMemcpyHostToDevice) != hipSuccess)
+    return W4V_ERR_HIP;
+  if (hipMemset(base + lay.counters_offset, 0, lay.counters_bytes) != hipSuccess) return W4V_ERR_HIP;
+  if (hipDeviceSynchronize() != hipSuccess) return W4V_ERR_HIP;
+  return W4V_OK;
+}
+
+int w4a16_chain(const void* x, int64_t ldx, void* y, int64_t ldy, int M, int K0, int N_last,
+                void* workspace, void* stream) {
+  if (M < 1 || K0 <= 0 || N_last <= 0) return W4V_ERR_INVALID_ARG;
+  if (M > w4v::kChainMaxRows) return W4V_ERR_UNSUPPORTED;
+  if (!x || !y || !workspace) return W4V_ERR_INVALID_ARG;
+  if (ldx < K0 || ldy < N_last) return W4V_ERR_INVALID_ARG;
+  if (!aligned(x, 16) || ldx % 8 != 0 || !aligned(y, 16) || ldy % 8 != 0 || !aligned(workspace, 256))
+    return W4V_ERR_ALIGNMENT;
+  const size_t xbytes = ((size_t)(M - 1) * (size_t)ldx + (size_t)K0) * 2;
+  const size_t ybytes = ((size_t)(M - 1) * (size_t)ldy + (size_t)N_last) * 2;
+  if (ranges_overlap(x, xbytes, y, ybytes)) return W4V_ERR_INVALID_ARG;
+  const int blocks = chain_blocks();
+  if (blocks <= 0) return W4V_ERR_HIP;
+  hipError_t e = w4v::launch_w4a16_chain(static_cast<w4v::ChainHeader*>(workspace),
+                                         static_cast<const _Float16*>(x), ldx,
+                                         static_cast<_Float16*>(y), ldy, M, K0, N_last, blocks,
+                                         static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? W4V_OK : W4V_ERR_HIP;
 }
 
 }  // extern "C"

@@ -208,12 +208,13 @@ __global__ __launch_bounds__(kThreads) void w4a16_skinny_kernel(GemmArgs a, int 
   const size_t ncols = (size_t)ntiles * kColTile;
   const size_t rows_blk = 16 * MT;
   float* pbase = partials + (size_t)mblk * splits * rows_blk * ncols;
+  const rsrc_t pr = make_rsrc(pbase);
 #pragma unroll
   for (int j = 0; j < MT; ++j) {
     const int mloc = row_of(j) - mbase;
-    float* p = pbase + ((size_t)split * rows_blk + mloc) * ncols + col;
-#pragma unroll
-    for (int c = 0; c < 4; ++c) st_agent(p + c, out[j][c]);
+    const f32x4 v = {out[j][0], out[j][1], out[j][2], out[j][3]};
+    st_agent_x4(pr, (uint32_t)((((size_t)split * rows_blk + mloc) * ncols + col) * 4),
+                __builtin_bit_cast(u32x4, v));
   }
   if (!arrive_last(tickets + (size_t)mblk * ntiles + tile, (unsigned)splits)) return;
 
@@ -221,14 +222,10 @@ __global__ __launch_bounds__(kThreads) void w4a16_skinny_kernel(GemmArgs a, int 
   for (int j = 0; j < MT; ++j) {
     const int m = row_of(j);
     const int mloc = m - mbase;
-    float s[4];
-#pragma unroll
-    for (int c = 0; c < 4; ++c) s[c] = ld_agent(pbase + (size_t)mloc * ncols + col + c);
-    for (int sp = 1; sp < splits; ++sp) {
-      const float* p = pbase + ((size_t)sp * rows_blk + mloc) * ncols + col;
-#pragma unroll
-      for (int c = 0; c < 4; ++c) s[c] += ld_agent(p + c);
-    }
+    f32x4 s = __builtin_bit_cast(f32x4, ld_agent_x4(pr, (uint32_t)(((size_t)mloc * ncols + col) * 4)));
+    for (int sp = 1; sp < splits; ++sp)
+      s += __builtin_bit_cast(
+          f32x4, ld_agent_x4(pr, (uint32_t)((((size_t)sp * rows_blk + mloc) * ncols + col) * 4)));
     if (colok && m < a.M)
       store_row4(a.y + (size_t)m * a.ldy + col, a.alpha * s[0], a.alpha * s[1], a.alpha * s[2],
                  a.alpha * s[3]);

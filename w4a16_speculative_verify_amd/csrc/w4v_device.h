@@ -19,6 +19,20 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
+// Pointers that were stored in LDS (or any memory) come back as generic
+// pointers, and generic (flat) loads count against both the vector-memory and
+// the LDS counters, so every LDS wait would also wait for them.  as_global()
+// restores the global address space for such pointers.
+#define W4V_GLOBAL __attribute__((address_space(1)))
+template <typename T>
+__device__ __forceinline__ const W4V_GLOBAL T* as_global(const T* p) {
+  return (const W4V_GLOBAL T*)(p);
+}
+template <typename T>
+__device__ __forceinline__ W4V_GLOBAL T* as_global_mut(T* p) {
+  return (W4V_GLOBAL T*)(p);
+}
+
 __device__ __forceinline__ f32x4 mfma16x16x32(const f16x8& a, const f16x8& b, const f32x4& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
@@ -125,6 +139,25 @@ __device__ __forceinline__ float ld_agent(const float* p) {
 }
 __device__ __forceinline__ int ld_agent(const int* p) {
   return __hip_atomic_load(const_cast<int*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Vector forms of the same agent-scope accesses, through buffer instructions
+// with the sc1 cache-policy bit (the bit the scalar forms above carry).  The
+// resource covers [base, base + 2 GiB); offsets are in bytes.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr int kSC1 = 16;
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, 0x7fffffff, 0x00020000);
+}
+__device__ __forceinline__ void st_agent_x4(rsrc_t r, uint32_t off, u32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, kSC1);
+}
+__device__ __forceinline__ void st_agent_x2(rsrc_t r, uint32_t off, u32x2 v) {
+  __builtin_amdgcn_raw_buffer_store_b64(v, r, off, 0, kSC1);
+}
+__device__ __forceinline__ u32x4 ld_agent_x4(rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kSC1);
 }
 
 // Takes the block's ticket on `ticket` after all of the block's agent-scope

@@ -70,6 +70,55 @@ LmheadPlan plan_lmhead(int M, int H, int V, int num_cus);
 hipError_t launch_lmhead_argmax(const LmheadArgs& a, const LmheadPlan& p, void* workspace,
                                 hipStream_t stream);
 
+// ---------------------------------------------------------------- chain of linears
+constexpr unsigned kChainMagic = 0x43563457u;   // "W4VC"
+constexpr int kChainWavesPerUnit = 7;           // math waves per block (plus one control wave)
+constexpr int kChainGroupsPerWave = 2;          // 128-k groups a math wave owns per unit
+constexpr int kChainMaxRows = 16;
+
+// Device-side header at offset 0 of a prepared chain workspace (256 bytes).
+struct ChainHeader {
+  unsigned magic;
+  unsigned n_linears;
+  unsigned total_units;
+  unsigned M;
+  unsigned work;         // unit dispenser (re-armed by the kernel)
+  unsigned exit_count;   // blocks that finished (re-armed by the kernel)
+  unsigned epoch;        // flags of the current launch hold epoch + 1
+  unsigned error;        // 1: a wait timed out, 2: workspace not prepared for this call
+  unsigned K0;           // width of the input rows
+  unsigned N_last;       // width of the output rows
+  unsigned pad0[2];
+  uint64_t lin_offset;   // byte offset of the ChainLinear table
+  uint64_t unit_offset;  // byte offset of the unit -> linear table (uint16)
+  unsigned pad1[48];
+};
+static_assert(sizeof(ChainHeader) == 256, "chain header is 256 bytes");
+
+struct ChainLinear {
+  const uint32_t* qweight;
+  const _Float16* scales;
+  const uint32_t* qzeros;
+  _Float16* out;         // fp16 [16 x ldo] output (unused for the last linear)
+  float* partials;       // fp32 [splits][16][ct*64] when splits > 1
+  unsigned* tickets;     // [ct] split arrivals per tile (splits > 1)
+  unsigned* flags;       // [ct] epoch + 1 once the tile's output is written
+  int K, N, ldo, splits, ct, unit0;
+  float alpha;
+  int pad;
+};
+
+struct ChainLayout {
+  size_t bytes;          // total workspace bytes
+  size_t lin_offset, unit_offset;
+  size_t counters_offset, counters_bytes;   // flags + tickets, zeroed by prepare
+  unsigned total_units;
+};
+
+hipError_t launch_w4a16_chain(ChainHeader* hdr, const _Float16* x, int64_t ldx, _Float16* y,
+                              int64_t ldy, int M, int K0, int N_last, int blocks,
+                              hipStream_t stream);
+
 // ---------------------------------------------------------------- verify
 hipError_t launch_greedy_verify(const int32_t* target_ids, const int32_t* draft_ids, int B, int K,
                                 int V, int32_t* accepted_len, int32_t* out_tokens,

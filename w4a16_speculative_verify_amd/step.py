@@ -17,7 +17,7 @@ from dataclasses import dataclass
 
 import torch
 
-from . import (gemm_workspace_size, lmhead_workspace_size, new_workspace, w4a16_gemm,
+from . import (Chain, gemm_workspace_size, lmhead_workspace_size, new_workspace, w4a16_gemm,
                w8a16_lmhead_argmax_verify)
 
 
@@ -33,7 +33,7 @@ class DeviceLinear:
 
 class VerifyStep:
     def __init__(self, linears, lm_w, lm_s, m: int, batch: int, k_draft: int,
-                 device="cuda"):
+                 device="cuda", chain: bool | None = None):
         if m != batch * (k_draft + 1):
             raise ValueError("rows must be batch * (k_draft + 1)")
         self.linears = list(linears)
@@ -55,6 +55,13 @@ class VerifyStep:
         if lm_w is not None:
             need = max(need, lmhead_workspace_size(m, lm_w.shape[1], lm_w.shape[0]))
         self.workspace = new_workspace(need, dev)
+        # one launch for the whole chain when the block fits the chain kernel
+        self.chain = None
+        if chain is None:
+            chain = False
+        if chain:
+            self.chain = Chain([(l.qweight, l.scales, l.qzeros, l.alpha) for l in self.linears],
+                               m, dev)
         self.target_ids = torch.empty(m, dtype=torch.int32, device=dev)
         self.max_logits = torch.empty(m, dtype=torch.float32, device=dev)
         self.accepted_len = torch.empty(batch, dtype=torch.int32, device=dev)
@@ -62,6 +69,8 @@ class VerifyStep:
 
     def linears_only(self, x: torch.Tensor) -> torch.Tensor:
         """Run the chain of linears on x (fp16 [m, >= k_in of the first]); returns the last output."""
+        if self.chain is not None:
+            return self.chain(x, out=self.out[-1])
         h = x
         for lin, y in zip(self.linears, self.out):
             w4a16_gemm(h[:, :lin.k_in], lin.qweight, lin.scales, lin.qzeros, alpha=lin.alpha,
