@@ -77,6 +77,8 @@ def main():
                     help="replays of the linears-only graph for the roofline timing")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="one device-to-device copy of this many MiB before timing (counter calibration)")
     ap.add_argument("--path", choices=["chain", "per-linear"], default="per-linear",
                     help="one persistent launch for all linears, or one launch per linear")
     args = ap.parse_args()
@@ -111,6 +113,13 @@ def main():
                       chain=args.path == "chain")
     x = up(wl.x)
     torch.cuda.synchronize()
+
+    if args.copy_probe_mib:
+        src = torch.empty(args.copy_probe_mib << 18, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     # target ids of this input (untimed), then one draft block per step
     no_drafts = torch.full((1, cfg.k_draft), -1, dtype=torch.int32, device=dev)

@@ -29,6 +29,10 @@ def run_gemm(w4v, x, lin, alpha=1.0, ws=None):
     (16, 9728, 2560),          # deep K (split across blocks)
     (16, 4096, 2560),
     (3, 9728, 1032),
+    (33, 256, 200),            # tiled path: one ragged row past a 32-row block
+    (130, 384, 136),           # tiled path: ragged rows and columns
+    (300, 1280, 1032),
+    (128, 128, 128),           # exactly one tile, one group
 ])
 def test_random_shapes(lib, m, k, n):
     log(f"gemm m={m} k={k} n={n}")
@@ -41,7 +45,7 @@ def test_random_shapes(lib, m, k, n):
 
 
 @pytest.mark.parametrize("enc", range(3))
-@pytest.mark.parametrize("m", [16, 21])
+@pytest.mark.parametrize("m", [16, 21, 64, 200])
 def test_identity_weights_bit_exact(lib, enc, m):
     n = 512
     eye = np.eye(n, dtype=np.int64)

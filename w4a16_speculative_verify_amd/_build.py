@@ -13,7 +13,7 @@ INCLUDE = os.path.join(ROOT, "include")
 OBJDIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libw4v.so")
 
-SOURCES = ["w4a16_skinny.hip", "w4a16_chain.hip", "w8a16_lmhead.hip", "greedy_verify.hip", "api.cpp"]
+SOURCES = ["w4a16_skinny.hip", "w4a16_tiled.hip", "w4a16_chain.hip", "w8a16_lmhead.hip", "greedy_verify.hip", "api.cpp"]
 
 # gfx950 only.  Packed-fp32 instructions are switched off for every HIP
 # translation unit (the host pass reports the feature as unknown; harmless).

@@ -184,6 +184,7 @@ int w4a16_gemm(const void* x, int64_t ldx, const int32_t* qweight, const void* s
   if (st != W4V_OK || M == 0 || N == 0) return st;
   const w4v::GemmPlan p = w4v::plan_w4a16(M, N, K, kPlanCUs);
   if (p.mblocks > kMaxGridYZ || p.splits > kMaxGridYZ) return W4V_ERR_UNSUPPORTED;
+  if (M >= w4v::kTiledMinRows && (M + 127) / 128 > kMaxGridYZ) return W4V_ERR_UNSUPPORTED;
   st = workspace_check(p.workspace_bytes(), workspace, workspace_bytes);
   if (st != W4V_OK) return st;
   w4v::GemmArgs a{};
@@ -198,7 +199,9 @@ int w4a16_gemm(const void* x, int64_t ldx, const int32_t* qweight, const void* s
   a.N = N;
   a.K = K;
   a.alpha = alpha;
-  hipError_t e = w4v::launch_w4a16_skinny(a, p, workspace, static_cast<hipStream_t>(stream));
+  hipError_t e = (M >= w4v::kTiledMinRows)
+                     ? w4v::launch_w4a16_tiled(a, static_cast<hipStream_t>(stream))
+                     : w4v::launch_w4a16_skinny(a, p, workspace, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? W4V_OK : W4V_ERR_HIP;
 }
 

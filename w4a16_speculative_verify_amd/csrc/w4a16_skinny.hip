@@ -251,10 +251,14 @@ GemmPlan plan_w4a16(int M, int N, int K, int num_cus) {
   const int gw_max = (p.mt == 1) ? 4 : 2;
   int splits = 1;
   if (p.mblocks == 1 && (size_t)p.col_tiles <= kMaxTickets) {
-    // enough splits that a wave holds at most gw_max groups, then more until
-    // the grid covers the chip twice, keeping at least one group per wave
+    // Enough splits that a wave holds at most gw_max groups.  Beyond that,
+    // about five splits measured best on MI355X for the 4B-class layer at
+    // M = 16 (QKV, O, gate+up and down all within 10% of their best), as long
+    // as every wave keeps at least one group.
     splits = (G + 4 * gw_max - 1) / (4 * gw_max);
-    const long target = 2L * num_cus;
+    const int pref = G / 4 < 5 ? G / 4 : 5;
+    if (pref > splits) splits = pref;
+    const long target = (long)num_cus / 2;
     while ((long)p.col_tiles * splits < target && G >= 4 * (splits + 1)) ++splits;
   }
   p.splits = splits;

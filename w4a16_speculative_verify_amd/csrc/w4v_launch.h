@@ -44,6 +44,9 @@ struct GemmPlan {
 GemmPlan plan_w4a16(int M, int N, int K, int num_cus);
 hipError_t launch_w4a16_skinny(const GemmArgs& a, const GemmPlan& p, void* workspace,
                                hipStream_t stream);
+// LDS-tiled MFMA GEMM for M > 32 rows (no workspace)
+hipError_t launch_w4a16_tiled(const GemmArgs& a, hipStream_t stream);
+constexpr int kTiledMinRows = 33;
 
 // ---------------------------------------------------------------- lm_head
 struct LmheadArgs {

@@ -67,42 +67,56 @@ __global__ __launch_bounds__(kThreads) void lmhead_argmax_kernel(LmheadArgs a, u
 #pragma unroll
       for (int t = 0; t < TILES; ++t) acc[mt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+    // rows past the vocabulary end read row 0 (their logits are never compared)
     const int8_t* wrow[TILES];
-    bool vok[TILES];
 #pragma unroll
     for (int t = 0; t < TILES; ++t) {
       const int v = v0 + 16 * t + (lane & 15);
-      vok[t] = v < a.V;
-      wrow[t] = a.w + (size_t)(vok[t] ? v : 0) * a.H + kb * 32;
+      wrow[t] = a.w + (size_t)(v < a.V ? v : 0) * a.H + kb * 32;
+    }
+    // hidden rows past M read row mbase and are zeroed at use
+    const int m_a = mbase + (lane & 15);
+    const _Float16* hrow[MT];
+    bool mok[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const int m = m_a + mt * 16;
+      mok[mt] = m < a.M;
+      hrow[mt] = a.h + (size_t)(mok[mt] ? m : mbase) * a.ldh + kb * 32;
     }
 
-    for (int ch = 0; ch < nchunks; ++ch) {
-      u32x4 wv[TILES][2];
+    // Two-deep software pipeline over 128-k chunks.  Per chunk the hidden
+    // rows (L2) are loaded before the next chunk's weights are requested, so
+    // waiting for them never waits for the prefetch.
+    u32x4 wa[TILES][2], wb[TILES][2];
+    auto load_w = [&](u32x4 (&dst)[TILES][2], int ch) {
 #pragma unroll
       for (int t = 0; t < TILES; ++t) {
+        // plain (cached) loads: each instruction uses half of every 128-byte line
+        // it touches and the next instruction the other half, which must still
+        // be in the L2 then
         const u32x4* p = reinterpret_cast<const u32x4*>(wrow[t] + ch * 128);
-        if (vok[t]) {
-          wv[t][0] = __builtin_nontemporal_load(p);
-          wv[t][1] = __builtin_nontemporal_load(p + 1);
-        } else {
-          wv[t][0] = u32x4{0u, 0u, 0u, 0u};
-          wv[t][1] = u32x4{0u, 0u, 0u, 0u};
-        }
+        dst[t][0] = p[0];
+        dst[t][1] = p[1];
       }
+    };
+    auto chunk = [&](const u32x4 (&wv)[TILES][2], int ch, bool prefetch, u32x4 (&nxt)[TILES][2]) {
       u32x4 hv[MT][4];
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
-        const int m = mbase + mt * 16 + (lane & 15);
-        const u32x4* p =
-            reinterpret_cast<const u32x4*>(a.h + (size_t)m * a.ldh + ch * 128 + kb * 32);
+        const u32x4* p = reinterpret_cast<const u32x4*>(hrow[mt] + ch * 128);
 #pragma unroll
-        for (int q = 0; q < 4; ++q) hv[mt][q] = (m < a.M) ? p[q] : u32x4{0u, 0u, 0u, 0u};
+        for (int q = 0; q < 4; ++q) hv[mt][q] = p[q];
       }
+      __builtin_amdgcn_sched_barrier(0);
+      if (prefetch) load_w(nxt, ch + 1);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         f16x8 av[MT];
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) av[mt] = __builtin_bit_cast(f16x8, hv[mt][q]);
+        for (int mt = 0; mt < MT; ++mt)
+          av[mt] = __builtin_bit_cast(f16x8, mok[mt] ? hv[mt][q] : u32x4{0u, 0u, 0u, 0u});
 #pragma unroll
         for (int t = 0; t < TILES; ++t) {
           const u32x4& src = wv[t][q >> 1];
@@ -112,6 +126,11 @@ __global__ __launch_bounds__(kThreads) void lmhead_argmax_kernel(LmheadArgs a, u
           for (int mt = 0; mt < MT; ++mt) acc[mt][t] = mfma16x16x32(av[mt], b, acc[mt][t]);
         }
       }
+    };
+    load_w(wa, 0);
+    for (int ch = 0; ch < nchunks; ch += 2) {
+      chunk(wa, ch, ch + 1 < nchunks, wb);
+      if (ch + 1 < nchunks) chunk(wb, ch + 1, ch + 2 < nchunks, wa);
     }
 
 #pragma unroll
