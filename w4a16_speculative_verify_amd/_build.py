@@ -17,9 +17,12 @@ SOURCES = ["w4a16_skinny.hip", "w4a16_tiled.hip", "w4a16_chain.hip", "w8a16_lmhe
 
 # gfx950 only.  Packed-fp32 instructions are switched off for every HIP
 # translation unit (the host pass reports the feature as unknown; harmless).
+# MFMA accumulators stay in ordinary VGPRs (no copies out of AGPRs before the
+# per-group scale is applied).
 HIP_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wall", "-Wno-unused-function",
 ]
 

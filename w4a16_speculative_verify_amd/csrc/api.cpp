@@ -174,6 +174,7 @@ size_t w4a16_gemm_workspace_size(int M, int N, int K, int group_size) {
   if (M <= 0 || N <= 0 || K <= 0 || group_size != w4v::kGroup || K % group_size != 0 ||
       N % 8 != 0)
     return 0;
+  if (M >= w4v::kTiledMinRows) return 0;
   return w4v::plan_w4a16(M, N, K, kPlanCUs).workspace_bytes();
 }
 
@@ -182,11 +183,19 @@ int w4a16_gemm(const void* x, int64_t ldx, const int32_t* qweight, const void* s
                float alpha, void* workspace, size_t workspace_bytes, void* stream) {
   int st = gemm_check(x, ldx, qweight, scales, qzeros, y, ldy, M, N, K, group_size);
   if (st != W4V_OK || M == 0 || N == 0) return st;
-  const w4v::GemmPlan p = w4v::plan_w4a16(M, N, K, kPlanCUs);
-  if (p.mblocks > kMaxGridYZ || p.splits > kMaxGridYZ) return W4V_ERR_UNSUPPORTED;
-  if (M >= w4v::kTiledMinRows && (M + 127) / 128 > kMaxGridYZ) return W4V_ERR_UNSUPPORTED;
-  st = workspace_check(p.workspace_bytes(), workspace, workspace_bytes);
-  if (st != W4V_OK) return st;
+  const bool tiled = M >= w4v::kTiledMinRows;
+  if (tiled && (M + 127) / 128 > kMaxGridYZ) return W4V_ERR_UNSUPPORTED;
+  w4v::GemmPlan p{};
+  if (!tiled) {
+    p = w4v::plan_w4a16(M, N, K, kPlanCUs);
+    // buffer resources take 32-bit offsets below 2 GiB
+    if ((size_t)K * N / 2 >= (1ull << 31) || (size_t)M * ldx * 2 >= (1ull << 31) ||
+        (size_t)K / 128 * N * 2 >= (1ull << 31) || p.mblocks > kMaxGridYZ ||
+        p.splits > kMaxGridYZ)
+      return W4V_ERR_UNSUPPORTED;
+    st = workspace_check(p.workspace_bytes(), workspace, workspace_bytes);
+    if (st != W4V_OK) return st;
+  }
   w4v::GemmArgs a{};
   a.x = static_cast<const _Float16*>(x);
   a.ldx = ldx;
@@ -199,9 +208,8 @@ int w4a16_gemm(const void* x, int64_t ldx, const int32_t* qweight, const void* s
   a.N = N;
   a.K = K;
   a.alpha = alpha;
-  hipError_t e = (M >= w4v::kTiledMinRows)
-                     ? w4v::launch_w4a16_tiled(a, static_cast<hipStream_t>(stream))
-                     : w4v::launch_w4a16_skinny(a, p, workspace, static_cast<hipStream_t>(stream));
+  hipError_t e = tiled ? w4v::launch_w4a16_tiled(a, static_cast<hipStream_t>(stream))
+                       : w4v::launch_w4a16_skinny(a, p, workspace, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? W4V_OK : W4V_ERR_HIP;
 }
 

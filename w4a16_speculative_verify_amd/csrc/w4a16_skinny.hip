@@ -2,25 +2,31 @@
 // K+1 rows, section 3 of the organisers' results page), gfx950.
 //
 // Work decomposition
-//   block  = 4 waves on one 64-column tile and one K-split; the waves divide
-//            the split's groups (128 k each) between them, at most GW each.
+//   block  = WT x WK waves: WT adjacent 64-column tiles x WK k-slices, on
+//            one K-split of the quantisation groups (128 k each).  The WT
+//            waves of a k-slice walk the same groups, so the activations of a
+//            group are loaded once per block and shared through LDS: on
+//            MI355X a CU's load throughput is the limit, and activations
+//            loaded per wave cost as much of it as the weights themselves.
 //   lane l = columns col..col+3 with col = tile*64 + 4*(l % 16), packed row
 //            4*it + l/16 of every 4-row quad; one 128-bit load brings 4 words
 //            = 4 columns x 8 k, the B operands of 4 MFMAs (one per column).
-//   A      = the activation rows, read straight from global memory (the block
-//            of rows is small and stays in L2), reordered in registers to the
-//            k order of the dequantised nibbles.
-// A wave issues the loads of all its groups (weights, zero-points, scales and
-// activations) before it computes anything, so the whole weight matrix is in
-// flight at once when the grid covers it: the skinny linear is bound by HBM
-// latency and bandwidth, not by arithmetic.
+//   A      = the group's 16 activation rows x 128 k: the k-slice's waves load
+//            it row-contiguous (4 rows x 256 bytes per instruction, 4/WT
+//            instructions each), reorder each 8-k chunk to the k order of the
+//            dequantised nibbles and store it in a double-buffered LDS tile,
+//            from which every wave reads the MFMA A layout.
+// Loads run D groups ahead of the math (a ring of register sets), and every
+// load is unconditional (a missing group reads zeros from outside its buffer
+// resource), because a load under a branch makes the compiler wait for all
+// loads in flight.
 // Per group the int4 words become exact fp16 (q - z); four 16x16x32 MFMAs per
 // column accumulate X * (q - z) over the group's 128 k in fp32, and the
 // group's fp16 scale is applied once to that fp32 sum (exact algebra: the
-// scale is constant over the group).  Waves of a block then add their fp32
-// results in fixed order through LDS; with split-K > 1 the blocks of a tile
-// publish fp32 partials and the last block to arrive adds them in split
-// order, so the output does not depend on arrival order.
+// scale is constant over the group).  The k-slices of a tile are added in
+// fixed order through LDS; with split-K > 1 the blocks of a tile publish fp32
+// partials and the last block to arrive adds them in split order, so the
+// output does not depend on arrival order.
 #include "w4v_device.h"
 #include "w4v_launch.h"
 
@@ -28,87 +34,53 @@ namespace w4v {
 
 namespace {
 
-constexpr int kWaves = 4;
-constexpr int kThreads = 64 * kWaves;
+constexpr int kMaxWaves = 8;
 
-template <int MT>
-struct GroupFrag {
-  u32x4 w[4];        // 4 quads of packed rows, 4 columns each
-  uint32_t zw;       // zero-point nibbles of the lane's 4 columns (low 16 bits)
-  u32x2 s;           // 4 fp16 scales
-  u32x4 a[MT][4];    // activations: per m-tile, per quad, 8 consecutive k
+struct Resources {
+  rsrc_t w, z, s, x;
 };
 
-template <int MT>
-__device__ __forceinline__ void load_group(GroupFrag<MT>& f, int g, const GemmArgs& a, int col,
-                                           bool colok, int kb, int row0) {
-  const int N = a.N;
-#pragma unroll
-  for (int it = 0; it < 4; ++it) {
-    if (colok) {
-      f.w[it] = __builtin_nontemporal_load(
-          reinterpret_cast<const u32x4*>(a.qweight + (size_t)(g * 16 + it * 4 + kb) * N + col));
-    } else {
-      f.w[it] = u32x4{0u, 0u, 0u, 0u};
-    }
-  }
-  if (colok) {
-    f.zw = a.qzeros[(size_t)g * (N >> 3) + (col >> 3)] >> ((col & 4) * 4);
-    f.s = *reinterpret_cast<const u32x2*>(a.scales + (size_t)g * N + col);
-  } else {
-    f.zw = 0u;
-    f.s = u32x2{0u, 0u};
-  }
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-    const int m = row0 + mt * 16;
-#pragma unroll
-    for (int it = 0; it < 4; ++it) {
-      if (m < a.M) {
-        f.a[mt][it] = *reinterpret_cast<const u32x4*>(a.x + (size_t)m * a.ldx + g * kGroup +
-                                                        it * 32 + kb * 8);
-      } else {
-        f.a[mt][it] = u32x4{0u, 0u, 0u, 0u};
-      }
-    }
-  }
-}
+// LDS tile of one group's activations: 16*MT rows of 128 fp16, padded by 16
+// bytes so that 8 lanes reading one 16-byte column hit distinct banks
+constexpr int kXRowWords = (kGroup * 2 + 16) / 4;
 
-template <int MT>
-__device__ __forceinline__ void compute_group(const GroupFrag<MT>& f, f32x4 (&acc)[MT][4],
-                                              uint32_t magic) {
-  ZeroPair zz[4];
+template <int MT, int WT>
+struct Frag {
+  static constexpr int kXLoads = 4 * MT / WT;   // activation loads of this wave per group
+  u32x4 w[4];            // 4 quads of packed rows, 4 columns each
+  uint32_t zw;           // zero-point word holding the lane's 4 columns at bit (l & 1) * 16
+  u32x2 s;               // 4 fp16 scales
+  u32x4 x[kXLoads];      // this wave's share of the group's activation rows
+};
+
+// Byte offsets of one lane's loads for group 0; group g adds g times the
+// per-group strides.  A group that does not exist gets 2 GiB added instead,
+// which puts every load outside its buffer resource (reads zeros, no memory
+// access): no load ever sits under a branch, because a load under a branch
+// makes the compiler wait for all loads in flight.
+template <int MT, int WT>
+struct Lanes {
+  uint32_t w, z, s;                     // weights (quad 0), zero-point word, scales
+  uint32_t x[Frag<MT, WT>::kXLoads];    // activation chunks
+  uint32_t wq;                          // weight offset step between quads (4 packed rows)
+  uint32_t gw, gz, gs;                  // per-group strides (activations: 256 bytes)
+};
+
+// activation load i of the group (i = 0 .. 4*MT-1): rows 4 i + l/16, k = 8 (l % 16) .. + 7
+__device__ __forceinline__ int xrow_of(int i, int lane) { return 4 * i + (lane >> 4); }
+
+template <int MT, int WT>
+__device__ __forceinline__ void load_group(Frag<MT, WT>& f, const Resources& rs,
+                                           const Lanes<MT, WT>& o, int g, bool valid) {
+  const uint32_t gg = (uint32_t)g;
 #pragma unroll
-  for (int c = 0; c < 4; ++c) zz[c] = zero_pair((f.zw >> (4 * c)) & 0xFu);
-  f32x4 tmp[MT][4];
+  for (int it = 0; it < 4; ++it)
+    f.w[it] = ld_x4<kNT>(rs.w, o.w + it * o.wq + (valid ? gg * o.gw : kNoLoad));
+  f.zw = ld_x1(rs.z, o.z + (valid ? gg * o.gz : kNoLoad));
+  f.s = ld_x2(rs.s, o.s + (valid ? gg * o.gs : kNoLoad));
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-    for (int c = 0; c < 4; ++c) tmp[mt][c] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int it = 0; it < 4; ++it) {
-    f16x8 av[MT];
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) av[mt] = permute_for_int4(f.a[mt][it]);
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const f16x8 b = dequant_int4_word(f.w[it][c], zz[c], magic);
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) tmp[mt][c] = mfma16x16x32(av[mt], b, tmp[mt][c]);
-    }
-  }
-  // copy the vector elements to scalars before the bit casts: a bit cast of
-  // an ext-vector element expression reads element 0 with this compiler
-  const uint32_t s_lo = f.s.x, s_hi = f.s.y;
-  const f16x2 s01 = __builtin_bit_cast(f16x2, s_lo);
-  const f16x2 s23 = __builtin_bit_cast(f16x2, s_hi);
-  const float sc[4] = {(float)s01.x, (float)s01.y, (float)s23.x, (float)s23.y};
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-    for (int c = 0; c < 4; ++c)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) acc[mt][c][r] = __builtin_fmaf(sc[c], tmp[mt][c][r], acc[mt][c][r]);
+  for (int q = 0; q < Frag<MT, WT>::kXLoads; ++q)
+    f.x[q] = ld_x4(rs.x, o.x[q] + (valid ? gg * (uint32_t)(kGroup * 2) : kNoLoad));
 }
 
 __device__ __forceinline__ void store_row4(_Float16* dst, float a0, float a1, float a2, float a3) {
@@ -118,28 +90,41 @@ __device__ __forceinline__ void store_row4(_Float16* dst, float a0, float a1, fl
   *reinterpret_cast<u32x2*>(dst) = v;
 }
 
-template <int MT, int GW>
-__global__ __launch_bounds__(kThreads) void w4a16_skinny_kernel(GemmArgs a, int splits,
-                                                                unsigned* tickets, float* partials) {
+template <int MT, int WT, int WK, int D>
+__global__ __launch_bounds__(64 * WT * WK) void w4a16_skinny_kernel(GemmArgs a, int splits,
+                                                                    unsigned* tickets,
+                                                                    float* partials) {
+  constexpr int NW = WT * WK;                       // waves per block
+  constexpr int kXWords = MT * 16 * kXRowWords;     // one group's activation tile
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int tile = blockIdx.x;
+  const int wt = wave % WT, wk = wave / WT;
+  const int cb = blockIdx.x;
   const int split = blockIdx.y;
   const int mblk = blockIdx.z;
   const int G = a.K / kGroup;
-
-  // groups of this split, then of this wave
-  const int gs0 = (int)((long long)G * split / splits);
-  const int gs1 = (int)((long long)G * (split + 1) / splits);
-  const int glen = gs1 - gs0;
-  const int g0 = gs0 + glen * wave / kWaves;
-  const int g1 = gs0 + glen * (wave + 1) / kWaves;
-
-  const int col = tile * kColTile + 4 * (lane & 15);
-  const bool colok = col < a.N;                    // N % 8 == 0: 4 columns all valid or none
-  const int kb = lane >> 4;
+  const int T = (a.N + kColTile - 1) / kColTile;
+  const int tile = cb * WT + wt;
+  const int kb = lane >> 4, chunk = lane & 15;
   const int mbase = mblk * 16 * MT;
-  const int row_a = mbase + (lane & 15);           // A-operand row of this lane (m-tile 0)
+
+  // groups of this split, then of this k-slice (G * splits < 2^31: 32-bit division)
+  const int gs0 = (int)((unsigned)(G * split) / (unsigned)splits);
+  const int gs1 = (int)((unsigned)(G * (split + 1)) / (unsigned)splits);
+  const int glen = gs1 - gs0;
+  const int g0 = gs0 + glen * wk / WK;
+  const int n = gs0 + glen * (wk + 1) / WK - g0;   // groups of this wave
+  const int nmax = (glen + WK - 1) / WK;            // steps of the block
+
+  const int col_raw = tile * kColTile + 4 * chunk;
+  const bool colok = tile < T && col_raw < a.N;     // N % 8 == 0: 4 columns all valid or none
+  const int col = colok ? col_raw : a.N - 4;        // the column this lane reads
+
+  constexpr int E = MT * 16;                        // accumulator floats per lane
+  constexpr int kTileWords = 2 * WK * kXWords;      // double-buffered activation tiles
+  constexpr int kRedWords = (WK > 1) ? NW * E * 64 : 0;
+  __shared__ uint32_t lds[kTileWords > kRedWords ? kTileWords : kRedWords];
+  auto xtile = [&](int buf, int slice) { return lds + (buf * WK + slice) * kXWords; };
 
   f32x4 acc[MT][4];
 #pragma unroll
@@ -147,96 +132,234 @@ __global__ __launch_bounds__(kThreads) void w4a16_skinny_kernel(GemmArgs a, int 
 #pragma unroll
     for (int c = 0; c < 4; ++c) acc[mt][c] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  Resources rs;
+  rs.w = make_rsrc(a.qweight);
+  rs.z = make_rsrc(a.qzeros);
+  rs.s = make_rsrc(a.scales);
+  rs.x = make_rsrc(a.x);
+  const uint32_t N = (uint32_t)a.N;
+  Lanes<MT, WT> o;
+  o.w = ((uint32_t)kb * N + col) * 4;
+  o.wq = 16 * N;                                    // 4 packed rows
+  o.gw = 64 * N;                                    // 16 packed rows
+  o.z = (uint32_t)(col >> 3) * 4;
+  o.gz = (N >> 3) * 4;
+  o.s = (uint32_t)col * 2;
+  o.gs = N * 2;
+#pragma unroll
+  for (int q = 0; q < Frag<MT, WT>::kXLoads; ++q) {
+    int m = mbase + xrow_of(q * WT + wt, lane);
+    m = m < a.M ? m : a.M - 1;                      // rows past M: never stored
+    o.x[q] = ((uint32_t)m * (uint32_t)a.ldx + chunk * 8) * 2;
+  }
   const uint32_t magic = in_vgpr(0x64006400u);
-  // batches of up to GW groups: all loads of a batch first, then the math
-  for (int gb = g0; gb < g1; gb += GW) {
-    GroupFrag<MT> f[GW];
+  const int zshift = (lane & 1) * 16;
+
+  Frag<MT, WT> f[D];
+  auto group_of = [&](int j) { return g0 + (j < n ? j : (n > 0 ? n - 1 : 0)); };
+  // prologue loads in the loop's order (f[0] complete, then f[1], ...): the
+  // wait counts at the loop head are then the same on entry and on the back edge
 #pragma unroll
-    for (int i = 0; i < GW; ++i)
-      if (gb + i < g1) load_group<MT>(f[i], gb + i, a, col, colok, kb, row_a);
-#pragma unroll
-    for (int i = 0; i < GW; ++i)
-      if (gb + i < g1) compute_group<MT>(f[i], acc, magic);
+  for (int i = 0; i < D; ++i) {
+    load_group<MT, WT>(f[i], rs, o, group_of(i), i < n);
+    __builtin_amdgcn_sched_barrier(0);
   }
 
-  // ---- combine the 4 waves in fixed order through LDS
-  // element e = (mt*4 + r)*4 + c of lane l sits at red[wave][e][l]
-  constexpr int E = MT * 16;
-  __shared__ float red[kWaves][E][64];
+  // Steps are padded to a multiple of D so that the loop body has no branch
+  // around loads or barriers (a padding step loads nothing and computes
+  // nothing); a branch there would make the compiler drain the loads at
+  // every iteration.
+  const int nsteps = (nmax + D - 1) / D * D;
+  for (int j0 = 0; j0 < nsteps; j0 += D) {
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
+    for (int i = 0; i < D; ++i) {
+      const int j = j0 + i;
+      // share the group's activations: this wave's chunks, reordered to the
+      // k order of the dequantised nibbles, into the LDS tile
+      uint32_t* xt = xtile(j & 1, wk);
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
+      for (int q = 0; q < Frag<MT, WT>::kXLoads; ++q)
+        *reinterpret_cast<f16x8*>(xt + xrow_of(q * WT + wt, lane) * kXRowWords + chunk * 4) =
+            permute_for_int4(f[i].x[q]);
+      lds_barrier();
+      if (j < n) {                                  // wave-uniform
+        ZeroPair zz[4];
 #pragma unroll
-      for (int c = 0; c < 4; ++c) red[wave][(mt * 4 + r) * 4 + c][lane] = acc[mt][c][r];
-  __syncthreads();
-
-  // wave w finishes rows (mt, r = w): MT rows per lane, 4 columns each
-  float out[MT][4];
+        for (int c = 0; c < 4; ++c) zz[c] = zero_pair((f[i].zw >> (zshift + 4 * c)) & 0xFu);
+        f32x4 tmp[MT][4];
 #pragma unroll
-  for (int j = 0; j < MT; ++j) {
-    const int mr = j * 4 + wave;      // (mt*4 + r)
+        for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      float s = red[0][mr * 4 + c][lane];
+          for (int c = 0; c < 4; ++c) tmp[mt][c] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int w = 1; w < kWaves; ++w) s += red[w][mr * 4 + c][lane];
-      out[j][c] = s;
+        for (int it = 0; it < 4; ++it) {
+          // A layout: row l % 16, k = 32 it + 8 (l / 16) .. + 7
+          f16x8 av[MT];
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt)
+            av[mt] = *reinterpret_cast<const f16x8*>(xt + (mt * 16 + chunk) * kXRowWords +
+                                                     (it * 4 + kb) * 4);
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            const f16x8 b = dequant_int4_word(f[i].w[it][c], zz[c], magic);
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) tmp[mt][c] = mfma16x16x32(av[mt], b, tmp[mt][c]);
+          }
+        }
+        // copy the vector elements to scalars before the bit casts: a bit
+        // cast of an ext-vector element expression reads element 0 with
+        // this compiler
+        const uint32_t s_lo = f[i].s.x, s_hi = f[i].s.y;
+        const f16x2 s01 = __builtin_bit_cast(f16x2, s_lo);
+        const f16x2 s23 = __builtin_bit_cast(f16x2, s_hi);
+        const float sc[4] = {(float)s01.x, (float)s01.y, (float)s23.x, (float)s23.y};
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+          for (int c = 0; c < 4; ++c)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              acc[mt][c][r] = __builtin_fmaf(sc[c], tmp[mt][c][r], acc[mt][c][r]);
+      }
+      load_group<MT, WT>(f[i], rs, o, group_of(j + D), j + D < n);
     }
   }
 
-  const int ntiles = gridDim.x;
-  auto row_of = [&](int j) {
-    const int mr = j * 4 + wave;
-    const int mt = mr >> 2, r = mr & 3;
-    return mbase + mt * 16 + 4 * (lane >> 4) + r;
-  };
+  // ---- add the k-slices of each tile in fixed order through LDS
+  // element e = (mt*4 + r)*4 + c of lane l of wave w sits at red[(w*E + e)*64 + l]
+  constexpr int kSlots = MT * 4;                    // (mt, r) row slots of a lane
+  constexpr int kMine = (kSlots + WK - 1) / WK;     // row slots this wave finishes (at most)
+  float* red = reinterpret_cast<float*>(lds);
+  float out[kMine][4];
+  if (WK == 1) {
+#pragma unroll
+    for (int j = 0; j < kMine; ++j)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) out[j][c] = acc[j >> 2][c][j & 3];
+  } else {
+    __syncthreads();                                // LDS tiles no longer read
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) red[(wave * E + (mt * 4 + r) * 4 + c) * 64 + lane] = acc[mt][c][r];
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < kMine; ++j) {
+      const int mr = j * WK + wk < kSlots ? j * WK + wk : kSlots - 1;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        float v = red[((0 * WT + wt) * E + mr * 4 + c) * 64 + lane];
+#pragma unroll
+        for (int k = 1; k < WK; ++k) v += red[((k * WT + wt) * E + mr * 4 + c) * 64 + lane];
+        out[j][c] = v;
+      }
+    }
+  }
+  // row slot j of this wave, or -1 when the k-slices outnumber the slots
+  auto slot_of = [&](int j) { return (WK == 1) ? j : (j * WK + wk < kSlots ? j * WK + wk : -1); };
+  auto row_of = [&](int mr) { return mbase + (mr >> 2) * 16 + 4 * kb + (mr & 3); };
 
   if (splits == 1) {
 #pragma unroll
-    for (int j = 0; j < MT; ++j) {
-      const int m = row_of(j);
-      if (colok && m < a.M)
+    for (int j = 0; j < kMine; ++j) {
+      const int mr = slot_of(j);
+      const int m = row_of(mr);
+      if (mr >= 0 && colok && m < a.M)
         store_row4(a.y + (size_t)m * a.ldy + col, a.alpha * out[j][0], a.alpha * out[j][1],
                    a.alpha * out[j][2], a.alpha * out[j][3]);
     }
     return;
   }
 
-  // ---- split-K: publish this block's partial, the last block of the tile reduces
-  // partials layout: [mblk][split][16*MT rows][ntiles*64 cols]
-  const size_t ncols = (size_t)ntiles * kColTile;
+  // ---- split-K: publish this block's partials, the last block of a tile adds them
+  // partials layout: [mblk][split][16*MT rows][col_blocks*WT*64 cols]
+  const size_t ncols = (size_t)gridDim.x * WT * kColTile;
   const size_t rows_blk = 16 * MT;
   float* pbase = partials + (size_t)mblk * splits * rows_blk * ncols;
   const rsrc_t pr = make_rsrc(pbase);
+  const int pcol = tile * kColTile + 4 * chunk;     // column in the partial rows (< ncols)
 #pragma unroll
-  for (int j = 0; j < MT; ++j) {
-    const int mloc = row_of(j) - mbase;
+  for (int j = 0; j < kMine; ++j) {
+    const int mr = slot_of(j);
+    if (mr < 0) continue;
+    const int mloc = row_of(mr) - mbase;
     const f32x4 v = {out[j][0], out[j][1], out[j][2], out[j][3]};
-    st_agent_x4(pr, (uint32_t)((((size_t)split * rows_blk + mloc) * ncols + col) * 4),
+    st_agent_x4(pr, (uint32_t)((((size_t)split * rows_blk + mloc) * ncols + pcol) * 4),
                 __builtin_bit_cast(u32x4, v));
   }
-  if (!arrive_last(tickets + (size_t)mblk * ntiles + tile, (unsigned)splits)) return;
+  // one ticket per tile of the block, taken after every partial store completed
+  __shared__ unsigned s_last[WT];
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x < WT) {
+    const int t = cb * WT + (int)threadIdx.x;
+    unsigned last = 0u;
+    if (t < T) {                                    // tiles past N take no ticket
+      unsigned* tk = tickets + (size_t)mblk * T + t;
+      const unsigned prev = __hip_atomic_fetch_add(tk, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (prev == (unsigned)splits - 1) {
+        __hip_atomic_store(tk, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        last = 1u;
+      }
+    }
+    s_last[threadIdx.x] = last;
+  }
+  __syncthreads();
+  if (!s_last[wt]) return;
 
 #pragma unroll
-  for (int j = 0; j < MT; ++j) {
-    const int m = row_of(j);
+  for (int j = 0; j < kMine; ++j) {
+    const int mr = slot_of(j);
+    if (mr < 0) continue;
+    const int m = row_of(mr);
     const int mloc = m - mbase;
-    f32x4 s = __builtin_bit_cast(f32x4, ld_agent_x4(pr, (uint32_t)(((size_t)mloc * ncols + col) * 4)));
-    for (int sp = 1; sp < splits; ++sp)
-      s += __builtin_bit_cast(
-          f32x4, ld_agent_x4(pr, (uint32_t)((((size_t)sp * rows_blk + mloc) * ncols + col) * 4)));
+    // partials in split order, eight loads in flight at a time
+    f32x4 sum = {0.f, 0.f, 0.f, 0.f};
+    for (int sp0 = 0; sp0 < splits; sp0 += 8) {
+      u32x4 v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int sp = sp0 + u < splits ? sp0 + u : splits - 1;
+        v[u] = ld_agent_x4(pr, (uint32_t)((((size_t)sp * rows_blk + mloc) * ncols + pcol) * 4));
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (sp0 + u < splits) sum += __builtin_bit_cast(f32x4, v[u]);
+    }
     if (colok && m < a.M)
-      store_row4(a.y + (size_t)m * a.ldy + col, a.alpha * s[0], a.alpha * s[1], a.alpha * s[2],
-                 a.alpha * s[3]);
+      store_row4(a.y + (size_t)m * a.ldy + col, a.alpha * sum[0], a.alpha * sum[1],
+                 a.alpha * sum[2], a.alpha * sum[3]);
   }
 }
 
-template <int MT, int GW>
+template <int MT, int WT, int WK, int D>
 void launch_t(const GemmArgs& a, const GemmPlan& p, unsigned* tickets, float* partials,
               hipStream_t stream) {
-  hipLaunchKernelGGL((w4a16_skinny_kernel<MT, GW>), dim3(p.col_tiles, p.splits, p.mblocks),
-                     dim3(kThreads), 0, stream, a, p.splits, tickets, partials);
+  hipLaunchKernelGGL((w4a16_skinny_kernel<MT, WT, WK, D>), dim3(p.col_blocks, p.splits, p.mblocks),
+                     dim3(64 * WT * WK), 0, stream, a, p.splits, tickets, partials);
+}
+
+template <int MT, int WT, int WK>
+void launch_wk(const GemmArgs& a, const GemmPlan& p, unsigned* tickets, float* partials,
+               hipStream_t stream) {
+  if (p.depth <= 2) launch_t<MT, WT, WK, 2>(a, p, tickets, partials, stream);
+  else launch_t<MT, WT, WK, 3>(a, p, tickets, partials, stream);
+}
+
+template <int MT>
+void launch_mt(const GemmArgs& a, const GemmPlan& p, unsigned* tickets, float* partials,
+               hipStream_t stream) {
+  switch (p.wt * 16 + p.wk) {
+    case 4 * 16 + 1: launch_wk<MT, 4, 1>(a, p, tickets, partials, stream); break;
+    case 2 * 16 + 2: launch_wk<MT, 2, 2>(a, p, tickets, partials, stream); break;
+    case 1 * 16 + 4: launch_wk<MT, 1, 4>(a, p, tickets, partials, stream); break;
+    case 8 * 16 + 1: launch_wk<MT, 8, 1>(a, p, tickets, partials, stream); break;
+    case 4 * 16 + 2: launch_wk<MT, 4, 2>(a, p, tickets, partials, stream); break;
+    case 2 * 16 + 4: launch_wk<MT, 2, 4>(a, p, tickets, partials, stream); break;
+    default: launch_wk<MT, 1, 8>(a, p, tickets, partials, stream); break;
+  }
 }
 
 }  // namespace
@@ -246,29 +369,29 @@ GemmPlan plan_w4a16(int M, int N, int K, int num_cus) {
   p.mt = (M <= 16) ? 1 : 2;
   const int rows_blk = 16 * p.mt;
   p.mblocks = (M + rows_blk - 1) / rows_blk;
-  p.col_tiles = (N + kColTile - 1) / kColTile;
+  p.tiles = (N + kColTile - 1) / kColTile;
   const int G = K / kGroup;
-  const int gw_max = (p.mt == 1) ? 4 : 2;
+  // Two tiles x two k-slices per block, and splits for about 192 blocks (3/4
+  // of the CUs: the split-K tail grows with the number of splits), keeping at
+  // least two groups per k-slice.  Measured best or within 5% of the best of
+  // the tile / k-slice / split choices on MI355X for the 4B-class verify
+  // shapes at M = 16 (QKV, O, gate+up, down).
+  p.wt = 2;
+  p.wk = 2;
+  p.col_blocks = (p.tiles + p.wt - 1) / p.wt;
   int splits = 1;
-  if (p.mblocks == 1 && (size_t)p.col_tiles <= kMaxTickets) {
-    // Enough splits that a wave holds at most gw_max groups.  Beyond that,
-    // about five splits measured best on MI355X for the 4B-class layer at
-    // M = 16 (QKV, O, gate+up and down all within 10% of their best), as long
-    // as every wave keeps at least one group.
-    splits = (G + 4 * gw_max - 1) / (4 * gw_max);
-    const int pref = G / 4 < 5 ? G / 4 : 5;
-    if (pref > splits) splits = pref;
-    const long target = (long)num_cus / 2;
-    while ((long)p.col_tiles * splits < target && G >= 4 * (splits + 1)) ++splits;
+  if ((size_t)p.tiles * p.mblocks <= kMaxTickets) {
+    const long blocks = (long)p.col_blocks * p.mblocks;
+    splits = (int)(192L * num_cus / 256 / blocks);
+    if (splits > G / (2 * p.wk)) splits = G / (2 * p.wk);
+    if (splits < 1) splits = 1;
   }
   p.splits = splits;
-  const int groups_per_block = (G + splits - 1) / splits;
-  const int per_wave = (groups_per_block + kWaves - 1) / kWaves;
-  p.gw = per_wave < gw_max ? per_wave : gw_max;
-  if (p.gw < 1) p.gw = 1;
+  p.depth = 3;
   if (splits > 1) {
     p.ticket_bytes = kTicketRegion;
-    p.partial_bytes = (size_t)p.mblocks * splits * rows_blk * p.col_tiles * kColTile * sizeof(float);
+    p.partial_bytes = (size_t)p.mblocks * splits * rows_blk * p.col_blocks * p.wt * kColTile *
+                      sizeof(float);
   }
   return p;
 }
@@ -281,17 +404,8 @@ hipError_t launch_w4a16_skinny(const GemmArgs& a, const GemmPlan& p, void* works
     tickets = static_cast<unsigned*>(workspace);
     partials = reinterpret_cast<float*>(static_cast<char*>(workspace) + p.ticket_bytes);
   }
-  if (p.mt == 1) {
-    switch (p.gw) {
-      case 1: launch_t<1, 1>(a, p, tickets, partials, stream); break;
-      case 2: launch_t<1, 2>(a, p, tickets, partials, stream); break;
-      case 3: launch_t<1, 3>(a, p, tickets, partials, stream); break;
-      default: launch_t<1, 4>(a, p, tickets, partials, stream); break;
-    }
-  } else {
-    if (p.gw == 1) launch_t<2, 1>(a, p, tickets, partials, stream);
-    else launch_t<2, 2>(a, p, tickets, partials, stream);
-  }
+  if (p.mt == 1) launch_mt<1>(a, p, tickets, partials, stream);
+  else launch_mt<2>(a, p, tickets, partials, stream);
   return hipGetLastError();
 }
 

@@ -160,6 +160,31 @@ __device__ __forceinline__ u32x4 ld_agent_x4(rsrc_t r, uint32_t off) {
   return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kSC1);
 }
 
+// Block barrier that orders LDS accesses only.  __syncthreads() also waits
+// for every global load in flight, which would drain a load pipeline at each
+// step; this one leaves them in flight.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// Plain buffer loads (cache policy Aux: 0, or kNT for streaming data).  An
+// offset at or past 2 GiB lies outside every resource made by make_rsrc and
+// reads zeros without touching memory: a branch-free way to skip a load.
+constexpr int kNT = 2;
+constexpr uint32_t kNoLoad = 0x80000000u;
+template <int Aux = 0>
+__device__ __forceinline__ u32x4 ld_x4(rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, Aux);
+}
+__device__ __forceinline__ u32x2 ld_x2(rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+}
+__device__ __forceinline__ uint32_t ld_x1(rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+}
+
 // Takes the block's ticket on `ticket` after all of the block's agent-scope
 // stores have completed.  True (in every thread) for the block that arrives
 // last of `count`; that block re-arms the counter to zero.

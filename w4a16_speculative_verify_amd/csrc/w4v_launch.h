@@ -33,9 +33,12 @@ struct GemmArgs {
 struct GemmPlan {
   int mt;            // 16-row m-tiles per block (1 or 2)
   int mblocks;       // blocks along M, each 16*mt rows
-  int col_tiles;     // ceil(N / 64)
+  int tiles;         // ceil(N / 64)
+  int wt;            // 64-column tiles per block (1, 2, 4 or 8)
+  int wk;            // k-slices per block (wt * wk = 4 or 8 waves)
+  int col_blocks;    // ceil(tiles / wt)
   int splits;        // split-K factor across blocks (1 = none)
-  int gw;            // groups a wave loads before computing (1..4)
+  int depth;         // groups in flight per wave (2 or 3)
   size_t ticket_bytes;
   size_t partial_bytes;
   size_t workspace_bytes() const { return ticket_bytes + partial_bytes; }
