@@ -70,7 +70,9 @@ int w4v_abi_version(void);
  *          y must not overlap x.
  * Sizes    M >= 0 (M == 0 or N == 0: nothing to do, W4V_OK), K > 0,
  *          N % 8 == 0, K % group_size == 0; group_size must be 128
- *          (W4V_ERR_UNSUPPORTED otherwise).
+ *          (W4V_ERR_UNSUPPORTED otherwise).  For M <= 32 the packed weights
+ *          (K*N/2 bytes), the scales and the rows of x (M*ldx*2 bytes) must
+ *          each stay below 2 GiB (W4V_ERR_UNSUPPORTED otherwise).
  * alpha    epilogue scale applied to the fp32 accumulator before the single
  *          round-to-nearest-even to fp16.
  * workspace  device memory of at least w4a16_gemm_workspace_size(M, N, K,
@@ -100,7 +102,9 @@ int w4a16_gemm(const void* x, int64_t ldx,
  * scales     fp16 [V], one scale per vocabulary row.
  * target_ids int32 [M] out.
  * max_logits fp32 [M] out (the winning logit), or NULL.
- * Sizes      M >= 0 (0: nothing to do), V > 0, H > 0 and H % 128 == 0.
+ * Sizes      M >= 0 (0: nothing to do), V > 0, H > 0 and H % 128 == 0;
+ *            V*H bytes of weights and M*ldh*2 bytes of h below 2 GiB
+ *            (W4V_ERR_UNSUPPORTED otherwise).
  * workspace  at least w8a16_lmhead_argmax_workspace_size(M, H, V) bytes,
  *            256-byte aligned, zeroed once.  Holds per-block (value, index)
  *            partials and an arrival counter.

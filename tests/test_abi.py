@@ -73,6 +73,9 @@ def gemm(lib, x=A, ldx=2560, qw=A, sc=A, qz=A, y=A * 64, ldy=2560, M=16, N=2560,
     (dict(y=A + 256), INVALID),                   # y overlaps x
     (dict(M=0), OK),                              # nothing to do: no launch
     (dict(N=0, ldy=0), OK),
+    # 32-bit buffer offsets of the skinny path: weights or x rows of 2 GiB or more
+    (dict(N=65536, K=65536, ldx=65536, ldy=65536, y=1 << 40), UNSUPPORTED),
+    (dict(ldx=1 << 26, y=1 << 40), UNSUPPORTED),
 ])
 def test_gemm_validation(lib, kw, status):
     assert gemm(lib, **kw) == status
@@ -108,6 +111,7 @@ def lm(lib, h=A, ldh=2560, w=A, sc=A, t=A, ml=None, M=16, H=2560, V=4096, ws=A *
     (dict(ws=None, wsb=0), WORKSPACE),
     (dict(wsb=16), WORKSPACE),
     (dict(M=0), OK),
+    (dict(H=1 << 16, ldh=1 << 16, V=1 << 15), UNSUPPORTED),   # 2 GiB of weights
 ])
 def test_lmhead_validation(lib, kw, status):
     assert lm(lib, **kw) == status

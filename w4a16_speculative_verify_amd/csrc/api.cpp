@@ -54,6 +54,9 @@ int lmhead_check(const void* h, int64_t ldh, const int8_t* w, const void* scales
   if (!aligned(h, 16) || (ldh % 8) != 0 || !aligned(w, 16) || !aligned(scales, 2) ||
       !aligned(target_ids, 4))
     return W4V_ERR_ALIGNMENT;
+  // buffer resources take 32-bit offsets below 2 GiB
+  if ((size_t)V * (size_t)H >= (1ull << 31) || (size_t)M * (size_t)ldh * 2 >= (1ull << 31))
+    return W4V_ERR_UNSUPPORTED;
   return W4V_OK;
 }
 

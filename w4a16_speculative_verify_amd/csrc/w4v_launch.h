@@ -65,7 +65,8 @@ struct LmheadArgs {
 struct LmheadPlan {
   int mt;            // 16-row m-tiles per block (1 or 2)
   int mblocks;
-  int tiles;         // 16-row vocabulary tiles per wave pass (1 or 4)
+  int tiles;         // 16-row vocabulary tiles per wave pass (1, 2 or 4)
+  int depth;         // steps in flight per wave (3, 4, 6 or 8)
   int vblocks;       // blocks along the vocabulary
   size_t ticket_bytes;
   size_t partial_bytes;

@@ -3,11 +3,19 @@
 // untied lm_head quantised to 8 bits, temperature-0 verification).
 //
 // Work decomposition
-//   wave pass = TILES x 16 vocabulary rows over the whole hidden width H.
-//     Lane l streams 32 consecutive bytes (k = 128*chunk + 32*(l/16) ..) of
-//     row v0 + 16*t + l%16 per 128-k chunk: two 128-bit loads per tile.  Each
-//     8-byte slice is the B operand of one 16x16x32 MFMA; the matching A slice
-//     is the same 8 k of the hidden rows, read from global memory (L2).
+//   wave pass = TILES x 16 vocabulary rows over the whole hidden width H, in
+//     steps of 128 k.  Lane l streams 32 consecutive bytes (k = 32*(l/16) ..)
+//     of row v0 + 16*t + l%16 per step: two 128-bit loads per tile.  Each
+//     8-byte slice is the B operand of one 16x16x32 MFMA.
+//   A (hidden rows) = one 128-k chunk per step, loaded once per block (one
+//     16-byte load per thread) into a double-buffered LDS tile that the four
+//     waves share: per-wave loads of it would cost a CU as much load
+//     throughput as half the weights.
+//   The block's passes are one sequence of steps streamed through a ring of
+//     D register sets; every load is unconditional (rows past V read row 0,
+//     steps past the block's work read zeros from outside the buffer
+//     resource), because a load under a branch makes the compiler wait for
+//     every load in flight.
 //   Logits stay in fp32 registers (never stored): logit = s8[v] * acc.
 //   Argmax: per lane running best over its columns (strict '>' keeps the
 //     lowest index because a lane's v only grows), then 16-lane butterflies
@@ -26,6 +34,9 @@ namespace {
 
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
+constexpr int kChunk = 128;                         // k per step
+constexpr int kHRowWords = (kChunk * 2 + 16) / 4;   // padded LDS row of the hidden chunk
+constexpr int kLmheadBlocksPerCU = 1;
 
 __device__ __forceinline__ void shfl_best(float& v, int& i, int mask) {
   const float ov = __shfl_xor(v, mask, 64);
@@ -37,6 +48,13 @@ __device__ __forceinline__ void shfl_best(float& v, int& i, int mask) {
 }
 
 template <int MT, int TILES>
+struct Step {
+  u32x4 w[TILES][2];     // 32 bytes of each tile row
+  u32x4 h[MT];           // this thread's 16 bytes of the hidden chunk
+  uint32_t sc[TILES];    // fp16 scale of each tile row (loaded with a pass's last step)
+};
+
+template <int MT, int TILES, int D>
 __global__ __launch_bounds__(kThreads) void lmhead_argmax_kernel(LmheadArgs a, unsigned* ticket,
                                                                  float* pval, int* pidx) {
   const int lane = threadIdx.x & 63;
@@ -44,9 +62,62 @@ __global__ __launch_bounds__(kThreads) void lmhead_argmax_kernel(LmheadArgs a, u
   const int kb = lane >> 4;
   const int mbase = blockIdx.y * 16 * MT;
   const int nvb = gridDim.x;
-  const int rows_per_pass = kWaves * TILES * 16;
-  const int npasses = (a.V + rows_per_pass - 1) / rows_per_pass;
-  const int nchunks = a.H / 128;
+  constexpr int kRowsPerPass = kWaves * TILES * 16;
+  // this block's vocabulary rows: an equal share [vb0, vb1), in passes
+  const int vb0 = (int)((long long)a.V * blockIdx.x / nvb);
+  const int vb1 = (int)((long long)a.V * (blockIdx.x + 1) / nvb);
+  const int my_passes = (vb1 - vb0 + kRowsPerPass - 1) / kRowsPerPass;
+  const int nchunks = a.H / kChunk;
+  const int nsteps = my_passes * nchunks;
+
+  constexpr int kHWords = MT * 16 * kHRowWords;
+  __shared__ uint32_t htile[2][kHWords];
+
+  const rsrc_t rw = make_rsrc(a.w);
+  const rsrc_t rh = make_rsrc(a.h);
+  const rsrc_t rs = make_rsrc(a.scales);
+  // hidden chunk: thread t loads row t / 16 (+16 per m-tile), 8 k at (t % 16) * 8
+  const int hr = threadIdx.x >> 4, hc = threadIdx.x & 15;
+  uint32_t hoff[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    int m = mbase + mt * 16 + hr;
+    m = m < a.M ? m : a.M - 1;                     // rows past M: never reported
+    hoff[mt] = ((uint32_t)m * (uint32_t)a.ldh + hc * 8) * 2;
+  }
+  // lane row of tile t in pass p; rows past the block's share load nothing
+  auto row_of = [&](int pass, int t) {
+    return vb0 + pass * kRowsPerPass + wave * TILES * 16 + 16 * t + (lane & 15);
+  };
+
+  auto load_step = [&](Step<MT, TILES>& f, int st) {
+    // Offsets are masked by OR-ing kNoLoad (bit 31) in, never by choosing
+    // between two loads: the compiler turns a select on a block-uniform
+    // condition into a branch around the load.
+    const int sc = st < nsteps ? st : 0;
+    const uint32_t skip = st < nsteps ? 0u : kNoLoad;
+    const int pass = sc / nchunks;
+    const int ch = sc - pass * nchunks;
+#pragma unroll
+    for (int t = 0; t < TILES; ++t) {
+      const int v = row_of(pass, t);
+      const uint32_t off = ((uint32_t)(v < vb1 ? v : 0) * (uint32_t)a.H + kb * 32 + ch * kChunk) |
+                           skip | (v < vb1 ? 0u : kNoLoad);
+      f.w[t][0] = ld_x4(rw, off);
+      f.w[t][1] = ld_x4(rw, off + 16);
+    }
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) f.h[mt] = ld_x4(rh, (hoff[mt] + ch * kChunk * 2) | skip);
+    // the row scales ride with the last step of a pass (a load at the pass end
+    // would wait for the whole ring)
+    const uint32_t not_last = ch == nchunks - 1 ? 0u : kNoLoad;
+#pragma unroll
+    for (int t = 0; t < TILES; ++t) {
+      const int v = row_of(pass, t);
+      f.sc[t] = __builtin_amdgcn_raw_buffer_load_b16(
+          rs, ((uint32_t)(v < vb1 ? v : 0) * 2) | skip | not_last | (v < vb1 ? 0u : kNoLoad), 0, 0);
+    }
+  };
 
   float best[MT][4];
   int bidx[MT][4];
@@ -57,98 +128,73 @@ __global__ __launch_bounds__(kThreads) void lmhead_argmax_kernel(LmheadArgs a, u
       best[mt][r] = -INFINITY;
       bidx[mt][r] = 0x7fffffff;
     }
+  f32x4 acc[MT][TILES];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int t = 0; t < TILES; ++t) acc[mt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  for (int pass = blockIdx.x; pass < npasses; pass += nvb) {
-    const int v0 = pass * rows_per_pass + wave * TILES * 16;
-    if (v0 >= a.V) break;      // waves past the vocabulary end have nothing to do
-    f32x4 acc[MT][TILES];
+  Step<MT, TILES> f[D];
+  // prologue in the loop's order, so the loop head's wait counts agree on entry
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
+  for (int i = 0; i < D; ++i) {
+    load_step(f[i], i);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  // steps padded to a multiple of D: no branch around loads or barriers
+  const int nsteps_pad = (nsteps + D - 1) / D * D;
+  for (int s0 = 0; s0 < nsteps_pad; s0 += D) {
 #pragma unroll
-      for (int t = 0; t < TILES; ++t) acc[mt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    // rows past the vocabulary end read row 0 (their logits are never compared)
-    const int8_t* wrow[TILES];
+    for (int i = 0; i < D; ++i) {
+      const int st = s0 + i;
+      uint32_t* ht = htile[st & 1];
 #pragma unroll
-    for (int t = 0; t < TILES; ++t) {
-      const int v = v0 + 16 * t + (lane & 15);
-      wrow[t] = a.w + (size_t)(v < a.V ? v : 0) * a.H + kb * 32;
-    }
-    // hidden rows past M read row mbase and are zeroed at use
-    const int m_a = mbase + (lane & 15);
-    const _Float16* hrow[MT];
-    bool mok[MT];
+      for (int mt = 0; mt < MT; ++mt)
+        *reinterpret_cast<u32x4*>(ht + (mt * 16 + hr) * kHRowWords + hc * 4) = f[i].h[mt];
+      lds_barrier();
+      if (st < nsteps) {                            // block-uniform
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      const int m = m_a + mt * 16;
-      mok[mt] = m < a.M;
-      hrow[mt] = a.h + (size_t)(mok[mt] ? m : mbase) * a.ldh + kb * 32;
-    }
-
-    // Two-deep software pipeline over 128-k chunks.  Per chunk the hidden
-    // rows (L2) are loaded before the next chunk's weights are requested, so
-    // waiting for them never waits for the prefetch.
-    u32x4 wa[TILES][2], wb[TILES][2];
-    auto load_w = [&](u32x4 (&dst)[TILES][2], int ch) {
+        for (int q = 0; q < 4; ++q) {
+          // A: row l % 16, k = 32 (l / 16) + 8 q .. + 7
+          f16x8 av[MT];
 #pragma unroll
-      for (int t = 0; t < TILES; ++t) {
-        // plain (cached) loads: each instruction uses half of every 128-byte line
-        // it touches and the next instruction the other half, which must still
-        // be in the L2 then
-        const u32x4* p = reinterpret_cast<const u32x4*>(wrow[t] + ch * 128);
-        dst[t][0] = p[0];
-        dst[t][1] = p[1];
-      }
-    };
-    auto chunk = [&](const u32x4 (&wv)[TILES][2], int ch, bool prefetch, u32x4 (&nxt)[TILES][2]) {
-      u32x4 hv[MT][4];
+          for (int mt = 0; mt < MT; ++mt)   // rows past M repeat row M - 1: never reported
+            av[mt] = *reinterpret_cast<const f16x8*>(ht + (mt * 16 + (lane & 15)) * kHRowWords +
+                                                     kb * 16 + q * 4);
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        const u32x4* p = reinterpret_cast<const u32x4*>(hrow[mt] + ch * 128);
+          for (int t = 0; t < TILES; ++t) {
+            const u32x4& src = f[i].w[t][q >> 1];
+            const u32x2 d = (q & 1) ? u32x2{src.z, src.w} : u32x2{src.x, src.y};
+            const f16x8 b = dequant_int8_x8(d);
 #pragma unroll
-        for (int q = 0; q < 4; ++q) hv[mt][q] = p[q];
-      }
-      __builtin_amdgcn_sched_barrier(0);
-      if (prefetch) load_w(nxt, ch + 1);
-      __builtin_amdgcn_sched_barrier(0);
+            for (int mt = 0; mt < MT; ++mt) acc[mt][t] = mfma16x16x32(av[mt], b, acc[mt][t]);
+          }
+        }
+        if (st % nchunks == nchunks - 1) {          // end of a pass: logits, argmax
+          const int pass = st / nchunks;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        f16x8 av[MT];
+          for (int t = 0; t < TILES; ++t) {
+            const int v = row_of(pass, t);
+            if (v < vb1) {
+              const uint32_t sbits = f[i].sc[t];
+              const float sv = (float)__builtin_bit_cast(_Float16, (uint16_t)sbits);
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-          av[mt] = __builtin_bit_cast(f16x8, mok[mt] ? hv[mt][q] : u32x4{0u, 0u, 0u, 0u});
+              for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-        for (int t = 0; t < TILES; ++t) {
-          const u32x4& src = wv[t][q >> 1];
-          const u32x2 d = (q & 1) ? u32x2{src.z, src.w} : u32x2{src.x, src.y};
-          const f16x8 b = dequant_int8_x8(d);
+                for (int r = 0; r < 4; ++r) {
+                  const float lg = sv * acc[mt][t][r];
+                  if (lg > best[mt][r]) {
+                    best[mt][r] = lg;
+                    bidx[mt][r] = v;
+                  }
+                }
+            }
 #pragma unroll
-          for (int mt = 0; mt < MT; ++mt) acc[mt][t] = mfma16x16x32(av[mt], b, acc[mt][t]);
+            for (int mt = 0; mt < MT; ++mt) acc[mt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+          }
         }
       }
-    };
-    load_w(wa, 0);
-    for (int ch = 0; ch < nchunks; ch += 2) {
-      chunk(wa, ch, ch + 1 < nchunks, wb);
-      if (ch + 1 < nchunks) chunk(wb, ch + 1, ch + 2 < nchunks, wa);
-    }
-
-#pragma unroll
-    for (int t = 0; t < TILES; ++t) {
-      const int v = v0 + 16 * t + (lane & 15);
-      if (v < a.V) {
-        const float s = (float)a.scales[v];
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const float lg = s * acc[mt][t][r];
-            if (lg > best[mt][r]) {
-              best[mt][r] = lg;
-              bidx[mt][r] = v;
-            }
-          }
-      }
+      load_step(f[i], st + D);
     }
   }
 
@@ -236,8 +282,24 @@ __global__ __launch_bounds__(kThreads) void lmhead_argmax_kernel(LmheadArgs a, u
 template <int MT, int TILES>
 void launch_t(const LmheadArgs& a, const LmheadPlan& p, unsigned* ticket, float* pval, int* pidx,
               hipStream_t stream) {
-  hipLaunchKernelGGL((lmhead_argmax_kernel<MT, TILES>), dim3(p.vblocks, p.mblocks),
-                     dim3(kThreads), 0, stream, a, ticket, pval, pidx);
+  switch (p.depth) {
+    case 3:
+      hipLaunchKernelGGL((lmhead_argmax_kernel<MT, TILES, 3>), dim3(p.vblocks, p.mblocks),
+                         dim3(kThreads), 0, stream, a, ticket, pval, pidx);
+      break;
+    case 4:
+      hipLaunchKernelGGL((lmhead_argmax_kernel<MT, TILES, 4>), dim3(p.vblocks, p.mblocks),
+                         dim3(kThreads), 0, stream, a, ticket, pval, pidx);
+      break;
+    case 6:
+      hipLaunchKernelGGL((lmhead_argmax_kernel<MT, TILES, 6>), dim3(p.vblocks, p.mblocks),
+                         dim3(kThreads), 0, stream, a, ticket, pval, pidx);
+      break;
+    default:
+      hipLaunchKernelGGL((lmhead_argmax_kernel<MT, TILES, 8>), dim3(p.vblocks, p.mblocks),
+                         dim3(kThreads), 0, stream, a, ticket, pval, pidx);
+      break;
+  }
 }
 
 }  // namespace
@@ -247,11 +309,15 @@ LmheadPlan plan_lmhead(int M, int H, int V, int num_cus) {
   LmheadPlan p{};
   p.mt = (M <= 16) ? 1 : 2;
   p.mblocks = (M + 16 * p.mt - 1) / (16 * p.mt);
-  // 64 rows per wave pass when the vocabulary fills the chip, else 16
-  p.tiles = ((long)V >= 64L * 4 * num_cus) ? 4 : 1;
+  // 32 rows per wave pass when the vocabulary fills the chip, else 16 (two
+  // tiles measured best on MI355X for the 151,936-row head; the ring depth,
+  // 3 to 8 steps, made no difference); the vocabulary is shared equally
+  // among one block per CU
+  p.tiles = ((long)V >= 32L * 4 * num_cus) ? 2 : 1;
+  p.depth = 3;
   const int rows_per_pass = kWaves * p.tiles * 16;
   const int npasses = (V + rows_per_pass - 1) / rows_per_pass;
-  p.vblocks = npasses < 4 * num_cus ? npasses : 4 * num_cus;
+  p.vblocks = npasses < kLmheadBlocksPerCU * num_cus ? npasses : kLmheadBlocksPerCU * num_cus;
   const size_t nblocks = (size_t)p.vblocks * p.mblocks;
   p.ticket_bytes = kTicketRegion;
   p.partial_bytes = align_up(nblocks * 16 * p.mt * sizeof(float), kWorkspaceAlign) +
@@ -269,9 +335,11 @@ hipError_t launch_lmhead_argmax(const LmheadArgs& a, const LmheadPlan& p, void* 
                                                      kWorkspaceAlign));
   if (p.mt == 1) {
     if (p.tiles == 4) launch_t<1, 4>(a, p, ticket, pval, pidx, stream);
+    else if (p.tiles == 2) launch_t<1, 2>(a, p, ticket, pval, pidx, stream);
     else launch_t<1, 1>(a, p, ticket, pval, pidx, stream);
   } else {
     if (p.tiles == 4) launch_t<2, 4>(a, p, ticket, pval, pidx, stream);
+    else if (p.tiles == 2) launch_t<2, 2>(a, p, ticket, pval, pidx, stream);
     else launch_t<2, 1>(a, p, ticket, pval, pidx, stream);
   }
   return hipGetLastError();
