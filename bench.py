@@ -30,6 +30,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+MFMA_FP16_PEAK_TFLOPS = 2500.0
 METRIC = "W4A16 verify GEMM HBM GB/s (% of peak) at M=16; verified tokens/s"
 
 
@@ -68,6 +69,57 @@ def cpu_baseline(wl, plan, drafts, min_seconds: float = 10.0):
                       f"oracle, {dt:.1f} s on {cores} threads"}
 
 
+def counter_traffic():
+    """HBM bytes per W4A16 launch from the committed counter summary, or None
+    when the kernel sources have changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "w4a16_skinny_traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+        h = hashlib.sha256()
+        for src in rec["sources"]:
+            with open(os.path.join(ROOT, src), "rb") as f:
+                h.update(f.read())
+    except (OSError, KeyError, ValueError):
+        return None
+    return rec["traffic_bytes_per_launch"] if h.hexdigest() == rec["sha256"] else None
+
+
+def prefill(dev, reps: int = 10):
+    """The prefill-shaped linears (gate+up 2560->19456, down 9728->2560) at
+    M = 2048 and 8192 through the LDS-tiled MFMA kernel: TFLOP/s per shape,
+    2*M*K*N flops over the average of ``reps`` back-to-back launches."""
+    import numpy as np
+    import torch
+
+    import gen
+    import w4a16_speculative_verify_amd as w4v
+
+    wl = gen.make_workload(5)
+    out = {}
+    for m in (2048, 8192):
+        for (k, n), lin, xa in zip(wl.cfg.single, wl.linears, wl.extra_x):
+            x = torch.from_numpy(np.ascontiguousarray(xa[:m])).to(dev)
+            qw, sc, qz = (torch.from_numpy(np.ascontiguousarray(t)).to(dev)
+                          for t in (lin.qweight, lin.scales, lin.qzeros))
+            y = torch.empty((m, n), dtype=torch.float16, device=dev)
+            w4v.w4a16_gemm(x, qw, sc, qz, out=y)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                w4v.w4a16_gemm(x, qw, sc, qz, out=y)
+            e1.record()
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1e3 / reps
+            tf = 2.0 * m * k * n / (us * 1e-6) / 1e12
+            out[f"m{m}_{k}x{n}"] = {"us": round(us, 2), "tflops": round(tf, 1),
+                                    "frac_of_fp16_mfma_peak": round(tf / MFMA_FP16_PEAK_TFLOPS, 4)}
+            del x, y
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -76,6 +128,8 @@ def main():
     ap.add_argument("--gemm-reps", type=int, default=50,
                     help="replays of the linears-only graph for the roofline timing")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true",
+                    help="skip the prefill-shaped (M = 2048 / 8192) GEMM timing")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="one device-to-device copy of this many MiB before timing (counter calibration)")
@@ -197,6 +251,12 @@ def main():
     gemm_gbs = lin_b / (lin_ms / 1e3) / 1e9
     step_gbs = (lin_b + lm_b) / (step_ms / 1e3) / 1e9
 
+    pre = None
+    if not args.no_prefill:
+        print("[bench] timing the prefill-shaped linears", file=sys.stderr, flush=True)
+        del g_step, g_lin
+        pre = prefill(dev)
+
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
@@ -230,11 +290,12 @@ def main():
         "wall_s_timed": round(wall, 4),
         "roofline": {"bound": "hbm", "achieved": round(gemm_gbs, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(gemm_gbs / HBM_PEAK_GBS, 4),
-                     "traffic": None,
-                     "kernel": "w4a16_skinny_kernel<1>",
+                     "traffic": counter_traffic(),
+                     "kernel": "w4a16_skinny_kernel (QKV, O, gate+up, down x 36 layers)",
                      "bytes_per_launch": round(lin_b / n_launch),
                      "avg_launch_us": round(act_launch_us, 3)},
         "cpu_baseline": cpu,
+        "prefill": pre,
     }
     print(json.dumps(out), flush=True)
 
