@@ -164,27 +164,35 @@ int w8a16_lmhead_argmax_verify(const void* h, int64_t ldh,
  * with W_l in the layout of w4a16_gemm.  Each intermediate output is rounded
  * to fp16 exactly as a separate w4a16_gemm call would round it.
  *
- * w4a16_chain_prepare writes the launch plan (unit tables, per-linear
- * buffers, counters) into the caller's workspace with synchronous copies; it
- * must not run while a call that uses this workspace is in flight.  The
- * prepared workspace is then used by any number of w4a16_chain calls ordered
- * on one stream (also from a captured graph: the kernel re-arms its own
- * counters).  The linears' device arrays must stay valid and unchanged.
+ * One block per compute unit stays resident for the whole chain; the plan
+ * gives every linear at most one unit (256 output columns x one K-split) per
+ * block, and linears are separated by a grid barrier.
+ *
+ * w4a16_chain_prepare writes the launch plan (per-linear descriptors,
+ * buffers, counters) for the current device's compute-unit count into the
+ * caller's workspace with synchronous copies; it must not run while a call
+ * that uses this workspace is in flight.  The prepared workspace is then used
+ * by any number of w4a16_chain calls ordered on one stream, on the same
+ * device (also from a captured graph: the kernel re-arms its own counters).
+ * The linears' device arrays must stay valid and unchanged.
  *
  * linears    host array of n_linears descriptors (device pointers inside),
  *            1 <= n_linears <= 65535; K % 128 == 0, N % 8 == 0, qweight and
- *            scales 16-byte aligned, qzeros 4-byte aligned.
+ *            scales 16-byte aligned, qzeros 4-byte aligned; K*N/2 below
+ *            2 GiB and N at most 256 columns per compute unit
+ *            (W4V_ERR_UNSUPPORTED otherwise).
  * M          1..16 rows (W4V_ERR_UNSUPPORTED above 16).
  * x          fp16 [M x K_0], row stride ldx >= K_0, 16-byte aligned, ldx % 8 == 0.
  * y          fp16 [M x N_{n-1}], row stride ldy >= N_{n-1}, 16-byte aligned,
  *            ldy % 8 == 0; must not overlap x.
  * workspace  w4a16_chain_workspace_size(...) bytes, 256-byte aligned.  Byte
  *            offset 28 holds an error word the kernel sets (sticky until the
- *            caller clears it): 1 = a dependency wait exceeded its bound
- *            (results invalid), 2 = the workspace was not prepared for this
- *            M, K_0 and N_{n-1} (nothing computed).
- * The work is handed out dynamically, and each output element is computed in
- * a fixed order, so results are bit-identical from call to call.
+ *            caller clears it): 1 = a barrier wait exceeded its bound
+ *            (results invalid; the workspace must be prepared again),
+ *            2 = the workspace was not prepared for this M, K_0, N_{n-1} and
+ *            device, or a previous call gave up a wait (nothing computed).
+ * Each output element is computed in a fixed order, so results are
+ * bit-identical from call to call.
  * ---------------------------------------------------------------------- */
 typedef struct {
   const int32_t* qweight;   /* int32 [K/8 x N]   */

@@ -13,9 +13,9 @@ pytestmark = pytest.mark.gpu
 
 # ChainLinear (w4v_launch.h): 7 pointers, 6 ints, float, int
 _LIN = np.dtype([("qweight", "<u8"), ("scales", "<u8"), ("qzeros", "<u8"), ("out", "<u8"),
-                 ("partials", "<u8"), ("tickets", "<u8"), ("flags", "<u8"), ("K", "<i4"),
-                 ("N", "<i4"), ("ldo", "<i4"), ("splits", "<i4"), ("ct", "<i4"),
-                 ("unit0", "<i4"), ("alpha", "<f4"), ("pad", "<i4")])
+                 ("partials", "<u8"), ("tickets", "<u8"), ("unused", "<u8"), ("K", "<i4"),
+                 ("N", "<i4"), ("ldo", "<i4"), ("splits", "<i4"), ("cb", "<i4"),
+                 ("units", "<i4"), ("alpha", "<f4"), ("pad", "<i4")])
 
 
 def intermediates(chain):

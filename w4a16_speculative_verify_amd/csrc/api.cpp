@@ -94,21 +94,32 @@ int run_lmhead(const void* h, int64_t ldh, const int8_t* w, const void* scales,
   return e == hipSuccess ? W4V_OK : W4V_ERR_HIP;
 }
 
-int chain_splits(int K) {
+// Split count of linear (K, N) for a grid of `blocks` blocks: as many units
+// (column blocks of 4 tiles x splits) as fit one per block, with about two
+// groups per split or more (one per k-slice) and every unit's activation
+// slice fitting in LDS.  0 when no split count fits.
+int chain_splits(int K, int N, int blocks) {
   const int G = K / w4v::kGroup;
-  const int per_unit = w4v::kChainWavesPerUnit * w4v::kChainGroupsPerWave;
-  return (G + per_unit - 1) / per_unit;
+  const int T = (N + w4v::kColTile - 1) / w4v::kColTile;
+  const int cb = (T + w4v::kChainTiles - 1) / w4v::kChainTiles;
+  const int s_min = (G + w4v::kChainMaxGroups - 1) / w4v::kChainMaxGroups;
+  const int s_max = G / w4v::kChainSlices > 1 ? G / w4v::kChainSlices : 1;
+  int s = blocks / cb;
+  if (s > s_max) s = s_max;
+  if (s < s_min) s = s_min;
+  if (s < 1 || s > G || (long)cb * s > blocks || (G + s - 1) / s > w4v::kChainMaxGroups) return 0;
+  return s;
 }
 
-// Checks the descriptors and lays out the workspace.  Host-only.
-int chain_layout(const w4v_chain_linear* lins, int n, int M, w4v::ChainLayout* lay) {
+// Checks the descriptors and lays out the workspace for a grid of `blocks`.  Host-only.
+int chain_layout(const w4v_chain_linear* lins, int n, int M, int blocks, w4v::ChainLayout* lay) {
   if (!lins || n < 1 || n > 65535) return W4V_ERR_INVALID_ARG;
   if (M < 1) return W4V_ERR_INVALID_ARG;
   if (M > w4v::kChainMaxRows) return W4V_ERR_UNSUPPORTED;
-  size_t off = 256;
+  if (blocks < 1) return W4V_ERR_HIP;
+  size_t off = sizeof(w4v::ChainHeader) + w4v::kChainBarBytes;
   lay->lin_offset = off;
   off += w4v::align_up((size_t)n * sizeof(w4v::ChainLinear), 256);
-  long long units = 0;
   for (int l = 0; l < n; ++l) {
     const w4v_chain_linear& L = lins[l];
     if (L.K <= 0 || L.N <= 0 || L.K % w4v::kGroup != 0 || L.N % 8 != 0) return W4V_ERR_INVALID_ARG;
@@ -116,26 +127,26 @@ int chain_layout(const w4v_chain_linear* lins, int n, int M, w4v::ChainLayout* l
     if (!L.qweight || !L.scales || !L.qzeros) return W4V_ERR_INVALID_ARG;
     if (!aligned(L.qweight, 16) || !aligned(L.scales, 16) || !aligned(L.qzeros, 4))
       return W4V_ERR_ALIGNMENT;
-    const int ct = (L.N + w4v::kColTile - 1) / w4v::kColTile;
-    units += (long long)ct * chain_splits(L.K);
+    // buffer resources take 32-bit offsets below 2 GiB
+    if ((size_t)L.K * L.N / 2 >= (1ull << 31)) return W4V_ERR_UNSUPPORTED;
+    if (chain_splits(L.K, L.N, blocks) == 0) return W4V_ERR_UNSUPPORTED;
   }
-  if (units >= (1LL << 31)) return W4V_ERR_UNSUPPORTED;
-  lay->total_units = (unsigned)units;
-  lay->unit_offset = off;
-  off += w4v::align_up((size_t)units * sizeof(uint16_t), 256);
   lay->counters_offset = off;
   size_t cnt = 0;
   for (int l = 0; l < n; ++l) {
-    const int ct = (lins[l].N + w4v::kColTile - 1) / w4v::kColTile;
-    cnt += w4v::align_up((size_t)2 * ct * sizeof(unsigned), 256);
+    const int T = (lins[l].N + w4v::kColTile - 1) / w4v::kColTile;
+    const int cb = (T + w4v::kChainTiles - 1) / w4v::kChainTiles;
+    cnt += (size_t)cb * w4v::kChainTiles * w4v::kChainSlot;   // one slot per tile's counter
   }
   lay->counters_bytes = cnt;
   off += cnt;
   for (int l = 0; l < n; ++l) {
-    const size_t ldo = (size_t)((lins[l].N + w4v::kColTile - 1) / w4v::kColTile) * w4v::kColTile;
+    const int T = (lins[l].N + w4v::kColTile - 1) / w4v::kColTile;
+    const int cb = (T + w4v::kChainTiles - 1) / w4v::kChainTiles;
+    const size_t ldo = (size_t)T * w4v::kColTile;
     if (l < n - 1) off += w4v::align_up(16 * ldo * 2, 256);
-    const int S = chain_splits(lins[l].K);
-    if (S > 1) off += w4v::align_up((size_t)S * 16 * ldo * 4, 256);
+    const int S = chain_splits(lins[l].K, lins[l].N, blocks);
+    if (S > 1) off += w4v::align_up((size_t)S * 16 * cb * w4v::kChainTiles * w4v::kColTile * 4, 256);
   }
   lay->bytes = off;
   return W4V_OK;
@@ -266,14 +277,15 @@ int w8a16_lmhead_argmax_verify(const void* h, int64_t ldh, const int8_t* w, cons
 
 size_t w4a16_chain_workspace_size(const w4v_chain_linear* linears, int n_linears, int M) {
   w4v::ChainLayout lay{};
-  if (chain_layout(linears, n_linears, M, &lay) != W4V_OK) return 0;
+  if (chain_layout(linears, n_linears, M, chain_blocks(), &lay) != W4V_OK) return 0;
   return lay.bytes;
 }
 
 int w4a16_chain_prepare(const w4v_chain_linear* linears, int n_linears, int M, void* workspace,
                         size_t workspace_bytes) {
+  const int blocks = chain_blocks();
   w4v::ChainLayout lay{};
-  int st = chain_layout(linears, n_linears, M, &lay);
+  int st = chain_layout(linears, n_linears, M, blocks, &lay);
   if (st != W4V_OK) return st;
   if (!workspace || workspace_bytes < lay.bytes) return W4V_ERR_WORKSPACE;
   if (!aligned(workspace, 256)) return W4V_ERR_ALIGNMENT;
@@ -282,35 +294,32 @@ int w4a16_chain_prepare(const w4v_chain_linear* linears, int n_linears, int M, v
   w4v::ChainHeader* hdr = reinterpret_cast<w4v::ChainHeader*>(img.data());
   hdr->magic = w4v::kChainMagic;
   hdr->n_linears = (unsigned)n_linears;
-  hdr->total_units = lay.total_units;
+  hdr->blocks = (unsigned)blocks;
   hdr->M = (unsigned)M;
   hdr->K0 = (unsigned)linears[0].K;
   hdr->N_last = (unsigned)linears[n_linears - 1].N;
   hdr->lin_offset = lay.lin_offset;
-  hdr->unit_offset = lay.unit_offset;
   w4v::ChainLinear* tab = reinterpret_cast<w4v::ChainLinear*>(img.data() + lay.lin_offset);
-  uint16_t* unit_lin = reinterpret_cast<uint16_t*>(img.data() + lay.unit_offset);
   size_t cnt_off = lay.counters_offset;
   size_t buf_off = lay.counters_offset + lay.counters_bytes;
-  unsigned u0 = 0;
   for (int l = 0; l < n_linears; ++l) {
     const w4v_chain_linear& L = linears[l];
     w4v::ChainLinear& d = tab[l];
-    const int ct = (L.N + w4v::kColTile - 1) / w4v::kColTile;
-    const int S = chain_splits(L.K);
+    const int T = (L.N + w4v::kColTile - 1) / w4v::kColTile;
+    const int cb = (T + w4v::kChainTiles - 1) / w4v::kChainTiles;
+    const int S = chain_splits(L.K, L.N, blocks);
     d.qweight = reinterpret_cast<const uint32_t*>(L.qweight);
     d.scales = static_cast<const _Float16*>(L.scales);
     d.qzeros = reinterpret_cast<const uint32_t*>(L.qzeros);
     d.K = L.K;
     d.N = L.N;
-    d.ct = ct;
+    d.cb = cb;
     d.splits = S;
-    d.unit0 = (int)u0;
+    d.units = cb * S;
     d.alpha = L.alpha;
-    d.ldo = ct * w4v::kColTile;
-    d.flags = reinterpret_cast<unsigned*>(base + cnt_off);
-    d.tickets = reinterpret_cast<unsigned*>(base + cnt_off + (size_t)ct * sizeof(unsigned));
-    cnt_off += w4v::align_up((size_t)2 * ct * sizeof(unsigned), 256);
+    d.ldo = T * w4v::kColTile;
+    d.tickets = reinterpret_cast<unsigned*>(base + cnt_off);
+    cnt_off += (size_t)cb * w4v::kChainTiles * w4v::kChainSlot;
     d.out = nullptr;
     if (l < n_linears - 1) {
       d.out = reinterpret_cast<_Float16*>(base + buf_off);
@@ -319,10 +328,8 @@ int w4a16_chain_prepare(const w4v_chain_linear* linears, int n_linears, int M, v
     d.partials = nullptr;
     if (S > 1) {
       d.partials = reinterpret_cast<float*>(base + buf_off);
-      buf_off += w4v::align_up((size_t)S * 16 * d.ldo * 4, 256);
+      buf_off += w4v::align_up((size_t)S * 16 * cb * w4v::kChainTiles * w4v::kColTile * 4, 256);
     }
-    for (int u = 0; u < ct * S; ++u) unit_lin[u0 + u] = (uint16_t)l;
-    u0 += (unsigned)(ct * S);
   }
   if (hipMemcpy(workspace, img.data(), img.size(), hipMemcpyHostToDevice) != hipSuccess)
     return W4V_ERR_HIP;

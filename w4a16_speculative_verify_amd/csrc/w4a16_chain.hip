@@ -1,43 +1,41 @@
 // A chain of W4A16 linears (the target's layers during one verify pass,
 // section 3 of the organisers' results page) in ONE persistent launch, gfx950.
 //
-// Why one launch: at M <= 16 rows a linear moves 5-25 MB, i.e. 0.7-3.1 us of
-// HBM time, while a launch costs several microseconds and every linear pays a
-// dependent chain of memory round trips.  Here the weights of the next unit
-// of work stream from HBM while the current unit waits for its activations,
-// and consecutive linears overlap through per-tile dataflow flags instead of
-// kernel boundaries.
+// Why one launch: at M <= 16 rows a linear moves 5-27 MB, 1-4 us of HBM time,
+// while a launch in a graph costs about 2.5 us on its own and every linear
+// also pays the ramp of a new grid and its split-K tail.  Here one block per
+// CU stays resident for all linears, the weights of the block's next unit are
+// requested before it waits for the previous linear to finish, and linears
+// are separated by a grid barrier instead of a kernel boundary.
 //
-// Work units.  Linear l is cut into ct(l) 64-column tiles and S(l) K-splits;
-// a unit is one (tile, split) pair.  Units are numbered linear by linear (all
-// splits of a tile adjacent) and handed out by an atomic counter, so a block
-// only ever waits for units that were handed out before its own: progress
-// does not depend on how many blocks are resident.
+// Work units.  Linear l is cut into cb column blocks of 4 tiles (256
+// columns) and S K-splits, cb * S <= blocks, and block b owns unit b of every
+// linear (a block with no unit in a linear only prefetches and waits).
 //
-// Roles inside a block (8 waves).  The memory counter of a wave (vmcnt) is
-// in-order, so a wave that waits for a late load also waits for every load
-// it issued earlier; the roles keep each wave's waits on its own stream:
-//   wave 0 ("control")   grabs and decodes units, polls the producer flags,
-//                        stores results, takes tickets, finishes split tiles;
-//   waves 1-7 ("math")   each own up to GW groups (128 k) of the unit: they
-//                        load the activations, then issue the raw int4 loads
-//                        of the NEXT unit, run the MFMAs on weights that were
-//                        dequantised during the previous unit, and then
-//                        dequantise the next unit's weights while the control
-//                        wave publishes.
-// Per unit: barrier A (unit decoded, producers done) -> activations + MFMA ->
-// barrier B -> all waves add the math waves' results in fixed order through
-// LDS -> barrier C -> control publishes: with one split it writes fp16 output
-// (alpha applied) and raises the tile's flag; otherwise it writes an fp32
-// partial and the last split to arrive adds the partials in split order,
-// writes the fp16 output and raises the flag.
-// Cross-XCD coherence: outputs, partials, flags and tickets are written with
-// agent-scope (sc1) stores and polled with agent-scope loads.  Every linear
-// writes a buffer of its own, which no block has read earlier in the launch,
-// so consumers may read activations through the L2.  Flags hold an epoch
-// number that advances at the end of every launch, so they never need
-// clearing; tickets and the work counter are re-armed by the kernel.
-// A wait that exceeds a bound sets the header's error word and gives up
+// A unit, 8 waves = 4 tiles x 2 k-slices:
+//   1. after the barrier, the unit's activation slice (16 rows x the split's
+//      groups) is loaded once, reordered to the nibble k order and stored in
+//      LDS, where all 8 waves read their MFMA A operands;
+//   2. each wave streams the packed weights of its tile and k-slice through a
+//      ring of 3 groups in flight (masked buffer loads, no branch around
+//      them), dequantises exactly and runs 16x16x32 MFMAs, the group scale
+//      applied once per group to the fp32 sum;
+//   3. the two k-slices of a tile are added through LDS; with one split the
+//      block writes the tile's fp16 output, otherwise it publishes an fp32
+//      partial and the last split to arrive (one ticket per tile) adds the
+//      partials in split order and writes the output.
+// Intermediate outputs go to buffers of the workspace with agent-scope (sc1)
+// stores; each linear writes a buffer of its own that nothing read earlier
+// in the launch, so the next linear may read it through the L2.
+// Grid barrier: after its stores have completed, a block adds itself to the
+// arrival counter of its group (16 groups); the last of a group re-arms that
+// counter and adds the group to the counter of finished groups; the last
+// group re-arms that one and writes the new generation to 16 copies, each
+// polled by one group's blocks with agent-scope loads.  Every counter and
+// copy has a 256-byte slot of its own: atomics and polls on one cache line
+// serialise at the memory side, which made a single-counter barrier take
+// several microseconds.  A poll that exceeds its bound sets the error and
+// abort words; every poller also watches its abort copy, so all blocks leave
 // instead of hanging.
 #include "w4v_device.h"
 #include "w4v_launch.h"
@@ -46,135 +44,83 @@ namespace w4v {
 
 namespace {
 
-constexpr int kWaves = 8;
-constexpr int kMathWaves = kWaves - 1;
-constexpr int kThreads = 64 * kWaves;
-constexpr int GW = kChainGroupsPerWave;
-constexpr unsigned kSpinLimit = 1u << 22;
+constexpr int WT = kChainTiles;
+constexpr int WK = kChainSlices;
+constexpr int kWaves = WT * WK;
+constexpr int kThreads = kChainThreads;
+constexpr int D = 3;                                // groups in flight per wave
+constexpr unsigned kSpinLimit = 1u << 20;
+// LDS row of one group's activations: 128 fp16 + 16 bytes of padding (8 lanes
+// reading one 16-byte column hit distinct banks)
+constexpr int kXRowWords = (kGroup * 2 + 16) / 4;
+constexpr int kXGroupWords = 16 * kXRowWords;
+constexpr int kXWords = kChainMaxGroups * kXGroupWords;
+constexpr int kRedWords = kWaves * 16 * 64;         // one fp32 accumulator set per wave
+constexpr int kLdsWords = kXWords > kRedWords ? kXWords : kRedWords;
 
-struct RawGroup {
-  u32x4 w[4];
-  uint32_t zw;       // the whole zero-point word (8 columns); the lane's 4 sit at `zshift`
-  u32x2 s;
+struct WFrag {
+  u32x4 w[4];        // 4 quads of packed rows, 4 columns each
+  uint32_t zw;       // zero-point word holding the lane's 4 columns at bit (l & 1) * 16
+  u32x2 s;           // 4 fp16 scales
 };
 
-// One decoded unit, shared through LDS.
-struct Unit {
-  int valid;
-  int lin, tile, split, splits;
-  int g0, g1;                 // groups of the unit's split
-  int K, N, ldo;
-  float alpha;
-  const uint32_t* qweight;
-  const _Float16* scales;
-  const uint32_t* qzeros;
-  const _Float16* xin;        // activations: input x or the previous linear's output
-  int64_t ldin;
-  _Float16* dst;              // fp16 output (y for the last linear)
-  int64_t ldd;
-  float* partials;
-  unsigned* tickets;
-  unsigned* flags;
-  const unsigned* dep_flags;  // flags of the previous linear (null for linear 0)
+// One unit as a block sees it.
+struct UnitPlan {
+  bool valid;
+  int cb, split, gs0, glen;       // column block, split, its groups
+  int g0, n;                      // this wave's groups (k-slice)
+  int col;                        // the column this lane reads (clamped below N)
+  bool colok;
+  uint32_t ow, oz, os;            // lane byte offsets for group 0
+  uint32_t gw, gz, gs;            // per-group strides
 };
 
-__device__ __forceinline__ void st_agent_u32(uint32_t* p, uint32_t v) {
-  __hip_atomic_store(as_global_mut(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+__device__ __forceinline__ UnitPlan plan_unit(const ChainLinear& L, int b, int wt, int wk, int lane) {
+  UnitPlan u{};
+  u.valid = b < L.units;
+  const int bb = u.valid ? b : 0;
+  u.cb = bb / L.splits;
+  u.split = bb - u.cb * L.splits;
+  const int G = L.K / kGroup;
+  u.gs0 = (int)((unsigned)(G * u.split) / (unsigned)L.splits);
+  u.glen = (int)((unsigned)(G * (u.split + 1)) / (unsigned)L.splits) - u.gs0;
+  u.g0 = u.gs0 + u.glen * wk / WK;
+  u.n = u.gs0 + u.glen * (wk + 1) / WK - u.g0;
+  if (!u.valid) u.n = 0;
+  const int T = (L.N + kColTile - 1) / kColTile;
+  const int tile = u.cb * WT + wt;
+  const int col_raw = tile * kColTile + 4 * (lane & 15);
+  u.colok = u.valid && tile < T && col_raw < L.N;
+  u.col = u.colok ? col_raw : L.N - 4;
+  const uint32_t N = (uint32_t)L.N;
+  u.ow = ((uint32_t)(lane >> 4) * N + u.col) * 4;
+  u.gw = 64 * N;
+  u.oz = (uint32_t)(u.col >> 3) * 4;
+  u.gz = (N >> 3) * 4;
+  u.os = (uint32_t)u.col * 2;
+  u.gs = N * 2;
+  return u;
 }
-__device__ __forceinline__ uint32_t ld_agent_u32(const uint32_t* p) {
-  return __hip_atomic_load(as_global_mut(const_cast<uint32_t*>(p)), __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
+
+// Weights, zero-points and scales of local group j of the wave (masked past n).
+__device__ __forceinline__ void load_w(WFrag& f, const rsrc_t& rw, const rsrc_t& rz,
+                                       const rsrc_t& rs, const UnitPlan& u, int j) {
+  const uint32_t g = (uint32_t)(u.g0 + (j < u.n ? j : 0));
+  const uint32_t skip = j < u.n ? 0u : kNoLoad;
+#pragma unroll
+  for (int it = 0; it < 4; ++it)
+    f.w[it] = ld_x4<kNT>(rw, (u.ow + it * (u.gw >> 2) + g * u.gw) | skip);
+  f.zw = ld_x1(rz, (u.oz + g * u.gz) | skip);
+  f.s = ld_x2(rs, (u.os + g * u.gs) | skip);
+}
+
+__device__ __forceinline__ void st_agent_u32(unsigned* p, unsigned v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 __device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
   const f16x2 h = {(_Float16)a, (_Float16)b};
   return __builtin_bit_cast(uint32_t, h);
-}
-
-// Groups [wg0, wg1) of math wave w (1..7): the unit's groups split as evenly
-// as possible, at most GW each.
-__device__ __forceinline__ void wave_groups(const Unit& u, int w, int& wg0, int& wg1) {
-  const int n = u.g1 - u.g0;
-  wg0 = u.g0 + n * (w - 1) / kMathWaves;
-  wg1 = u.g0 + n * w / kMathWaves;
-}
-
-// Control wave: fill `u` for unit index `idx` (all lanes compute it; lane 0 writes).
-__device__ __forceinline__ void decode(Unit& u, int idx, int total, const ChainLinear* lins,
-                                       const uint16_t* unit_lin, int nlin, const _Float16* x,
-                                       int64_t ldx, _Float16* y, int64_t ldy) {
-  Unit d{};
-  d.valid = idx < total;
-  if (d.valid) {
-    d.lin = unit_lin[idx];
-    const ChainLinear& L = lins[d.lin];
-    const int j = idx - L.unit0;
-    d.splits = L.splits;
-    d.tile = j / L.splits;
-    d.split = j - d.tile * L.splits;
-    const int G = L.K / kGroup;
-    d.g0 = (int)((long long)G * d.split / L.splits);
-    d.g1 = (int)((long long)G * (d.split + 1) / L.splits);
-    d.K = L.K;
-    d.N = L.N;
-    d.ldo = L.ldo;
-    d.alpha = L.alpha;
-    d.qweight = L.qweight;
-    d.scales = L.scales;
-    d.qzeros = L.qzeros;
-    d.partials = L.partials;
-    d.tickets = L.tickets;
-    d.flags = L.flags;
-    if (d.lin == 0) {
-      d.xin = x;
-      d.ldin = ldx;
-      d.dep_flags = nullptr;
-    } else {
-      const ChainLinear& P = lins[d.lin - 1];
-      d.xin = P.out;
-      d.ldin = P.ldo;
-      d.dep_flags = P.flags;
-    }
-    if (d.lin == nlin - 1) {
-      d.dst = y;
-      d.ldd = ldy;
-    } else {
-      d.dst = L.out;
-      d.ldd = L.ldo;
-    }
-  }
-  if ((threadIdx.x & 63) == 0) u = d;
-}
-
-// Branch-free raw loads: every lane always loads from a valid address (the
-// caller clamps group and column), so the compiler can count the loads that
-// are still in flight exactly and wait only for the ones it needs.
-__device__ __forceinline__ void load_raw(RawGroup& r, const Unit& u, int g, int col, int kb) {
-  const int N = u.N;
-#pragma unroll
-  for (int it = 0; it < 4; ++it)
-    r.w[it] = __builtin_nontemporal_load(as_global(
-        reinterpret_cast<const u32x4*>(u.qweight + (size_t)(g * 16 + it * 4 + kb) * N + col)));
-  r.zw = *as_global(u.qzeros + (size_t)g * (N >> 3) + (col >> 3));
-  r.s = *as_global(reinterpret_cast<const u32x2*>(u.scales + (size_t)g * N + col));
-}
-
-struct Deq {
-  f16x8 b[4][4];   // [quad][column]
-  uint32_t s01, s23;   // the four fp16 group scales, packed
-};
-
-__device__ __forceinline__ void dequant(Deq& d, const RawGroup& r, int zshift, uint32_t magic) {
-  ZeroPair zz[4];
-  const uint32_t zw = r.zw >> zshift;
-#pragma unroll
-  for (int c = 0; c < 4; ++c) zz[c] = zero_pair((zw >> (4 * c)) & 0xFu);
-#pragma unroll
-  for (int it = 0; it < 4; ++it)
-#pragma unroll
-    for (int c = 0; c < 4; ++c) d.b[it][c] = dequant_int4_word(r.w[it][c], zz[c], magic);
-  d.s01 = r.s.x;
-  d.s23 = r.s.y;
 }
 
 __global__ __launch_bounds__(kThreads) void w4a16_chain_kernel(ChainHeader* hdr,
@@ -184,258 +130,273 @@ __global__ __launch_bounds__(kThreads) void w4a16_chain_kernel(ChainHeader* hdr,
                                                                int N_last) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int kb = lane >> 4;
+  const int wt = wave % WT, wk = wave / WT;
+  const int kb = lane >> 4, chunk = lane & 15;
+  const int b = blockIdx.x;
 
-  __shared__ Unit s_unit[2];
-  __shared__ unsigned s_epoch;
-  __shared__ float red[kMathWaves][16][64];
-  __shared__ float red2[16][64];
-
-  // a workspace that was not prepared for this shape: report and touch nothing else
+  // a workspace that was not prepared for this call: report and touch nothing else
   if (hdr->magic != kChainMagic || (int)hdr->M != M_arg || (int)hdr->K0 != K0 ||
-      (int)hdr->N_last != N_last) {
-    if (threadIdx.x == 0 && blockIdx.x == 0) st_agent_u32(&hdr->error, 2u);
+      (int)hdr->N_last != N_last || hdr->blocks != gridDim.x || hdr->abort != 0u) {
+    if (threadIdx.x == 0 && b == 0) st_agent_u32(&hdr->error, 2u);
     return;
   }
-  const ChainLinear* lins = reinterpret_cast<const ChainLinear*>(
-      reinterpret_cast<const char*>(hdr) + hdr->lin_offset);
-  const uint16_t* unit_lin = reinterpret_cast<const uint16_t*>(
-      reinterpret_cast<const char*>(hdr) + hdr->unit_offset);
-  const int total = (int)hdr->total_units;
-  const int M = (int)hdr->M;
+  const ChainLinear* lins =
+      reinterpret_cast<const ChainLinear*>(reinterpret_cast<const char*>(hdr) + hdr->lin_offset);
   const int nlin = (int)hdr->n_linears;
+  const int M = (int)hdr->M;
+  const unsigned nblk = gridDim.x;
 
-  // ---- prologue: the control wave takes two units
-  int grabbed = 0;   // control wave: unit index obtained for iteration + 2
-  if (wave == 0) {
-    int u0 = 0, u1 = 0;
-    if (lane == 0) {
-      s_epoch = ld_agent_u32(&hdr->epoch);
-      u0 = (int)__hip_atomic_fetch_add(&hdr->work, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      u1 = (int)__hip_atomic_fetch_add(&hdr->work, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-    u0 = __shfl(u0, 0, 64);
-    u1 = __shfl(u1, 0, 64);
-    decode(s_unit[0], u0, total, lins, unit_lin, nlin, x, ldx, y, ldy);
-    decode(s_unit[1], u1, total, lins, unit_lin, nlin, x, ldx, y, ldy);
+  __shared__ uint32_t lds[kLdsWords];
+  __shared__ unsigned s_flag[WT + 1];
+  __shared__ unsigned s_gen0;
+  // barrier slots: group counters, finished-group counter, generation copies
+  char* const bar = reinterpret_cast<char*>(hdr) + sizeof(ChainHeader);
+  auto slot = [&](int i) { return reinterpret_cast<unsigned*>(bar + (size_t)i * kChainSlot); };
+  const int ngroups = (int)nblk < kChainBarGroups ? (int)nblk : kChainBarGroups;
+  const int grp = b % kChainBarGroups;
+  unsigned* const my_gen = slot(kChainBarGroups + 1 + grp);
+  if (threadIdx.x == 0) {
+    s_gen0 = __hip_atomic_load(my_gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_flag[WT] = 0u;
   }
   __syncthreads();
-  const unsigned target = s_epoch + 1;
-  const uint32_t magic = in_vgpr(0x64006400u);
+  const unsigned gen0 = s_gen0;
 
-  // math waves: the first unit's raw loads; its first group is dequantised
-  // ahead, the second stays raw and is dequantised quad by quad next to the MFMAs
-  Deq deq0;
-  RawGroup raw1;
-  // the lane's 4 columns in the zero-point word: nibbles 0-3 or 4-7
+  const uint32_t magic = in_vgpr(0x64006400u);
   const int zshift = (lane & 1) * 16;
-  if (wave > 0 && s_unit[0].valid) {
-    const Unit& u = s_unit[0];
-    int wg0, wg1;
-    wave_groups(u, wave, wg0, wg1);
-    const int col = min(u.tile * kColTile + 4 * (lane & 15), u.N - 4);
-    RawGroup r0;
-    load_raw(r0, u, wg0 < wg1 ? wg0 : u.g0, col, kb);
-    load_raw(raw1, u, wg0 + 1 < wg1 ? wg0 + 1 : u.g0, col, kb);
-    dequant(deq0, r0, zshift, magic);
+
+  // weights of linear 0 in flight before anything else
+  ChainLinear L = lins[0];
+  UnitPlan u = plan_unit(L, b, wt, wk, lane);
+  rsrc_t rw = make_rsrc(L.qweight), rz = make_rsrc(L.qzeros), rs = make_rsrc(L.scales);
+  WFrag f[D];
+#pragma unroll
+  for (int i = 0; i < D; ++i) {
+    load_w(f[i], rw, rz, rs, u, i);
+    __builtin_amdgcn_sched_barrier(0);
   }
 
-  for (int it = 0;; ++it) {
-    Unit& cu = s_unit[it & 1];
-    Unit& nu = s_unit[(it + 1) & 1];
+  for (int l = 0; l < nlin; ++l) {
+    const _Float16* xin = l == 0 ? x : lins[l - 1].out;
+    const int64_t ldin = l == 0 ? ldx : lins[l - 1].ldo;
+    const bool last_lin = l == nlin - 1;
 
-    // ---- control: grab unit it+2 (result used after publishing), wait for producers
-    if (wave == 0) {
-      if (lane == 0 && cu.valid)
-        grabbed = (int)__hip_atomic_fetch_add(&hdr->work, 1u, __ATOMIC_RELAXED,
-                                              __HIP_MEMORY_SCOPE_AGENT);
-      if (cu.valid && cu.dep_flags) {
-        const int t0 = cu.g0 * (kGroup / kColTile);
-        const int nt = (cu.g1 - cu.g0) * (kGroup / kColTile);
-        bool ok = lane >= nt;
+    // ---- wait for linear l-1 (grid barrier l-1), unless this block released it
+    if (l > 0) {
+      if (threadIdx.x == 0 && s_flag[WT] == 0u) {
+        const unsigned target = gen0 + (unsigned)l;
+        const rsrc_t rh = make_rsrc(my_gen);
         unsigned spins = 0;
         while (true) {
-          if (!ok) ok = ld_agent_u32(cu.dep_flags + t0 + lane) == target;
-          if (__all(ok)) break;
+          const u32x2 g = __builtin_amdgcn_raw_buffer_load_b64(rh, 0, 0, kSC1);   // generation, abort
+          if (g.x == target) break;
+          if (g.y != 0u) { s_flag[WT] = 2u; break; }
           if (++spins > kSpinLimit) {
-            if (lane == 0) st_agent_u32(&hdr->error, 1u);
+            st_agent_u32(&hdr->error, 1u);
+            st_agent_u32(&hdr->abort, 1u);
+            for (int c = 0; c < kChainBarGroups; ++c) st_agent_u32(slot(kChainBarGroups + 1 + c) + 1, 1u);
+            s_flag[WT] = 2u;
             break;
           }
-          __builtin_amdgcn_s_sleep(1);
+          __builtin_amdgcn_s_sleep(2);
         }
       }
+      lds_barrier();
+      if (s_flag[WT] == 2u) return;                 // a wait gave up somewhere: leave
     }
-    __syncthreads();                                         // A
-    if (!cu.valid) break;
 
-    // ---- math: activations, then the next unit's raw loads, then the MFMAs
-    RawGroup rn0, rn1;
-    int nwg0 = 0, nwg1 = 0;
-    if (wave > 0) {
-      int wg0, wg1;
-      wave_groups(cu, wave, wg0, wg1);
-      u32x4 av[GW][4];
-      const int m = lane & 15;
-      const bool mok = m < M;
+    if (u.valid) {
+      // ---- the unit's activation slice into LDS: rows x groups x 16 chunks of 8 k
       {
-        // branch-free: invalid rows or groups read row 0 / the unit's first group
-        const _Float16* xr = cu.xin + (size_t)(mok ? m : 0) * cu.ldin + kb * 8;
+        const rsrc_t rx = make_rsrc(xin);
+        const int nchunks = 16 * u.glen * 16;
+        constexpr int kMaxPer = kChainMaxGroups * 256 / kThreads;
+        u32x4 v[kMaxPer];
 #pragma unroll
-        for (int i = 0; i < GW; ++i) {
-          const int g = (wg0 + i < wg1) ? wg0 + i : cu.g0;
+        for (int i = 0; i < kMaxPer; ++i) {
+          const int c = (int)threadIdx.x + i * kThreads;
+          const int gl = c >> 8, row = (c >> 4) & 15, ch = c & 15;
+          const int m = row < M ? row : M - 1;
+          const uint32_t off = ((uint32_t)m * (uint32_t)ldin + (u.gs0 + gl) * kGroup + ch * 8) * 2;
+          v[i] = ld_x4(rx, c < nchunks ? off : kNoLoad);
+        }
 #pragma unroll
-          for (int q = 0; q < 4; ++q)
-            av[i][q] = *as_global(reinterpret_cast<const u32x4*>(xr + g * kGroup + q * 32));
+        for (int i = 0; i < kMaxPer; ++i) {
+          const int c = (int)threadIdx.x + i * kThreads;
+          if (c < nchunks) {
+            const int gl = c >> 8, row = (c >> 4) & 15, ch = c & 15;
+            *reinterpret_cast<f16x8*>(lds + gl * kXGroupWords + row * kXRowWords + ch * 4) =
+                permute_for_int4(v[i]);
+          }
         }
       }
-      // keep every activation load ahead of the prefetch in the wave's in-order
-      // memory counter, so waiting for the activations never waits for the prefetch
-      __builtin_amdgcn_sched_barrier(0);
-      {
-        // next unit's raw weights (or a harmless re-read of this unit's first group)
-        const Unit& u = nu.valid ? nu : cu;
-        int a0, a1;
-        wave_groups(u, wave, a0, a1);
-        nwg0 = nu.valid ? a0 : 0;
-        nwg1 = nu.valid ? a1 : 0;
-        const int ncol = min(u.tile * kColTile + 4 * (lane & 15), u.N - 4);
-        load_raw(rn0, u, a0 < a1 ? a0 : u.g0, ncol, kb);
-        load_raw(rn1, u, a0 + 1 < a1 ? a0 + 1 : u.g0, ncol, kb);
-      }
-      __builtin_amdgcn_sched_barrier(0);
+      lds_barrier();
+
+      // ---- this wave's groups: weights through the ring, activations from LDS
       f32x4 acc[4];
 #pragma unroll
       for (int c = 0; c < 4; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
-      if (wg0 < wg1) {
-        f32x4 tmp[4];
+      const int nsteps = (u.n + D - 1) / D * D;
+      for (int j0 = 0; j0 < nsteps; j0 += D) {
 #pragma unroll
-        for (int c = 0; c < 4; ++c) tmp[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int i = 0; i < D; ++i) {
+          const int j = j0 + i;
+          if (j < u.n) {
+            const uint32_t* xt = lds + (u.g0 - u.gs0 + j) * kXGroupWords;
+            ZeroPair zz[4];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const f16x8 a = permute_for_int4(mok ? av[0][q] : u32x4{0u, 0u, 0u, 0u});
+            for (int c = 0; c < 4; ++c) zz[c] = zero_pair((f[i].zw >> (zshift + 4 * c)) & 0xFu);
+            f32x4 tmp[4];
 #pragma unroll
-          for (int c = 0; c < 4; ++c) tmp[c] = mfma16x16x32(a, deq0.b[q][c], tmp[c]);
+            for (int c = 0; c < 4; ++c) tmp[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int it = 0; it < 4; ++it) {
+              const f16x8 av = *reinterpret_cast<const f16x8*>(xt + chunk * kXRowWords + (it * 4 + kb) * 4);
+#pragma unroll
+              for (int c = 0; c < 4; ++c)
+                tmp[c] = mfma16x16x32(av, dequant_int4_word(f[i].w[it][c], zz[c], magic), tmp[c]);
+            }
+            // copy the vector elements to scalars before the bit casts: a bit
+            // cast of an ext-vector element expression reads element 0 with
+            // this compiler
+            const uint32_t s_lo = f[i].s.x, s_hi = f[i].s.y;
+            const f16x2 s01 = __builtin_bit_cast(f16x2, s_lo);
+            const f16x2 s23 = __builtin_bit_cast(f16x2, s_hi);
+            const float sc[4] = {(float)s01.x, (float)s01.y, (float)s23.x, (float)s23.y};
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+#pragma unroll
+              for (int r = 0; r < 4; ++r) acc[c][r] = __builtin_fmaf(sc[c], tmp[c][r], acc[c][r]);
+          }
+          load_w(f[i], rw, rz, rs, u, j + D);
         }
-        const f16x2 s01 = __builtin_bit_cast(f16x2, deq0.s01);
-        const f16x2 s23 = __builtin_bit_cast(f16x2, deq0.s23);
-        const float sc[4] = {(float)s01.x, (float)s01.y, (float)s23.x, (float)s23.y};
-#pragma unroll
-        for (int c = 0; c < 4; ++c)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) acc[c][r] = sc[c] * tmp[c][r];
       }
-      if (wg0 + 1 < wg1) {
-        ZeroPair zz[4];
-        const uint32_t zw = raw1.zw >> zshift;
-#pragma unroll
-        for (int c = 0; c < 4; ++c) zz[c] = zero_pair((zw >> (4 * c)) & 0xFu);
-        f32x4 tmp[4];
-#pragma unroll
-        for (int c = 0; c < 4; ++c) tmp[c] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const f16x8 a = permute_for_int4(mok ? av[1][q] : u32x4{0u, 0u, 0u, 0u});
-#pragma unroll
-          for (int c = 0; c < 4; ++c)
-            tmp[c] = mfma16x16x32(a, dequant_int4_word(raw1.w[q][c], zz[c], magic), tmp[c]);
-        }
-        const uint32_t s_lo = raw1.s.x, s_hi = raw1.s.y;
-        const f16x2 s01 = __builtin_bit_cast(f16x2, s_lo);
-        const f16x2 s23 = __builtin_bit_cast(f16x2, s_hi);
-        const float sc[4] = {(float)s01.x, (float)s01.y, (float)s23.x, (float)s23.y};
-#pragma unroll
-        for (int c = 0; c < 4; ++c)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) acc[c][r] = __builtin_fmaf(sc[c], tmp[c][r], acc[c][r]);
-      }
+
+      // ---- the two k-slices of each tile, in fixed order through LDS
+      float* red = reinterpret_cast<float*>(lds);
+      lds_barrier();                                // activation slice no longer read
 #pragma unroll
       for (int r = 0; r < 4; ++r)
 #pragma unroll
-        for (int c = 0; c < 4; ++c) red[wave - 1][r * 4 + c][lane] = acc[c][r];
-    }
-    __syncthreads();                                         // B
-
-    // ---- all waves: fixed-order sum of the math waves, (r, c) pairs 2*wave and 2*wave+1
+        for (int c = 0; c < 4; ++c) red[(wave * 16 + r * 4 + c) * 64 + lane] = acc[c][r];
+      lds_barrier();
+      // wave (wt, wk) finishes rows r = 2 j + wk (j = 0, 1) of its tile: 4 kb + r
+      float out[2][4];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int e = 2 * wave + j;
-      float s = red[0][e][lane];
+      for (int j = 0; j < 2; ++j) {
+        const int r = 2 * j + wk;
 #pragma unroll
-      for (int w = 1; w < kMathWaves; ++w) s += red[w][e][lane];
-      red2[e][lane] = s;
-    }
-    __syncthreads();                                         // C
-
-    if (wave == 0) {
-      // ---- control: publish unit `cu` (vector agent-scope stores: 4 columns per lane and row)
-      const int col = cu.tile * kColTile + 4 * (lane & 15);
-      const bool colok = col < cu.N;
-      const rsrc_t dr = make_rsrc(cu.dst);
-      if (cu.splits == 1) {
+        for (int c = 0; c < 4; ++c) {
+          float v = red[((0 * WT + wt) * 16 + r * 4 + c) * 64 + lane];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int m = 4 * kb + r;
-          if (colok && m < M) {
-            const u32x2 v = {pack_f16x2(cu.alpha * red2[r * 4 + 0][lane], cu.alpha * red2[r * 4 + 1][lane]),
-                             pack_f16x2(cu.alpha * red2[r * 4 + 2][lane], cu.alpha * red2[r * 4 + 3][lane])};
-            st_agent_x2(dr, (uint32_t)(((size_t)m * cu.ldd + col) * 2), v);
-          }
-        }
-        __builtin_amdgcn_s_waitcnt(0);
-        if (lane == 0) st_agent_u32(cu.flags + cu.tile, target);
-      } else {
-        const size_t pld = (size_t)cu.ldo;
-        const rsrc_t pr = make_rsrc(cu.partials);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const f32x4 v = {red2[r * 4 + 0][lane], red2[r * 4 + 1][lane], red2[r * 4 + 2][lane],
-                           red2[r * 4 + 3][lane]};
-          st_agent_x4(pr, (uint32_t)((((size_t)cu.split * 16 + 4 * kb + r) * pld + col) * 4),
-                      __builtin_bit_cast(u32x4, v));
-        }
-        __builtin_amdgcn_s_waitcnt(0);
-        unsigned t = 0;
-        if (lane == 0)
-          t = __hip_atomic_fetch_add(as_global_mut(cu.tickets + cu.tile), 1u, __ATOMIC_RELAXED,
-                                     __HIP_MEMORY_SCOPE_AGENT);
-        t = __shfl(t, 0, 64);
-        if (t == (unsigned)(cu.splits - 1)) {
-          if (lane == 0) st_agent_u32(cu.tickets + cu.tile, 0u);
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int m = 4 * kb + r;
-            f32x4 f = __builtin_bit_cast(f32x4, ld_agent_x4(pr, (uint32_t)(((size_t)m * pld + col) * 4)));
-            for (int sp = 1; sp < cu.splits; ++sp)
-              f += __builtin_bit_cast(
-                  f32x4, ld_agent_x4(pr, (uint32_t)((((size_t)sp * 16 + m) * pld + col) * 4)));
-            if (colok && m < M) {
-              const u32x2 v = {pack_f16x2(cu.alpha * f[0], cu.alpha * f[1]),
-                               pack_f16x2(cu.alpha * f[2], cu.alpha * f[3])};
-              st_agent_x2(dr, (uint32_t)(((size_t)m * cu.ldd + col) * 2), v);
-            }
-          }
-          __builtin_amdgcn_s_waitcnt(0);
-          if (lane == 0) st_agent_u32(cu.flags + cu.tile, target);
+          for (int k = 1; k < WK; ++k) v += red[((k * WT + wt) * 16 + r * 4 + c) * 64 + lane];
+          out[j][c] = v;
         }
       }
-      // ---- control: decode unit it+2 into the slot `cu` leaves free
-      const int g2 = __shfl(grabbed, 0, 64);
-      decode(cu, g2, total, lins, unit_lin, nlin, x, ldx, y, ldy);
-    } else if (nu.valid) {
-      // ---- math: dequantise the next unit's first group while the control wave publishes
-      if (nwg0 < nwg1) dequant(deq0, rn0, zshift, magic);
-      if (nwg0 + 1 < nwg1) raw1 = rn1;
+      _Float16* dst = last_lin ? y : L.out;
+      const int64_t ldd = last_lin ? ldy : L.ldo;
+      const rsrc_t rd = make_rsrc(dst);
+      auto store_out = [&](int m, float a0, float a1, float a2, float a3) {
+        const u32x2 v = {pack_f16x2(L.alpha * a0, L.alpha * a1), pack_f16x2(L.alpha * a2, L.alpha * a3)};
+        const uint32_t off = (uint32_t)(((size_t)m * ldd + u.col) * 2);
+        if (last_lin) __builtin_amdgcn_raw_buffer_store_b64(v, rd, off, 0, 0);
+        else st_agent_x2(rd, off, v);
+      };
+      if (L.splits == 1) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int m = 4 * kb + 2 * j + wk;
+          if (u.colok && m < M) store_out(m, out[j][0], out[j][1], out[j][2], out[j][3]);
+        }
+      } else {
+        // partials [split][16 rows][cb * 4 * 64 columns]
+        const size_t ncols = (size_t)L.cb * WT * kColTile;
+        const rsrc_t pr = make_rsrc(L.partials);
+        const int pcol = (u.cb * WT + wt) * kColTile + 4 * chunk;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int m = 4 * kb + 2 * j + wk;
+          const f32x4 v = {out[j][0], out[j][1], out[j][2], out[j][3]};
+          st_agent_x4(pr, (uint32_t)((((size_t)u.split * 16 + m) * ncols + pcol) * 4),
+                      __builtin_bit_cast(u32x4, v));
+        }
+        __builtin_amdgcn_s_waitcnt(0);              // this thread's partial stores are complete
+        lds_barrier();
+        if (threadIdx.x < WT) {
+          const int t = u.cb * WT + (int)threadIdx.x;
+          const int T = (L.N + kColTile - 1) / kColTile;
+          unsigned last = 0u;
+          if (t < T) {
+            unsigned* tk = L.tickets + (size_t)t * (kChainSlot / sizeof(unsigned));
+            const unsigned prev =
+                __hip_atomic_fetch_add(tk, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (prev == (unsigned)L.splits - 1) {
+              __hip_atomic_store(tk, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+              last = 1u;
+            }
+          }
+          s_flag[threadIdx.x] = last;
+        }
+        lds_barrier();
+        if (s_flag[wt]) {
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            const int m = 4 * kb + 2 * j + wk;
+            f32x4 sum = {0.f, 0.f, 0.f, 0.f};
+            for (int sp0 = 0; sp0 < L.splits; sp0 += 8) {
+              u32x4 v[8];
+#pragma unroll
+              for (int q = 0; q < 8; ++q) {
+                const int sp = sp0 + q < L.splits ? sp0 + q : L.splits - 1;
+                v[q] = ld_agent_x4(pr, (uint32_t)((((size_t)sp * 16 + m) * ncols + pcol) * 4));
+              }
+#pragma unroll
+              for (int q = 0; q < 8; ++q)
+                if (sp0 + q < L.splits) sum += __builtin_bit_cast(f32x4, v[q]);
+            }
+            if (u.colok && m < M) store_out(m, sum[0], sum[1], sum[2], sum[3]);
+          }
+        }
+      }
     }
-  }
+    if (last_lin) break;
 
-  // the last block out re-arms the work counter and advances the epoch
-  if (threadIdx.x == 0) {
-    const unsigned e =
-        __hip_atomic_fetch_add(&hdr->exit_count, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (e == gridDim.x - 1) {
-      st_agent_u32(&hdr->work, 0u);
-      st_agent_u32(&hdr->exit_count, 0u);
-      st_agent_u32(&hdr->epoch, target);
+    // ---- arrive at barrier l once every store of the block has completed,
+    //      then request the next linear's weights while waiting
+    __builtin_amdgcn_s_waitcnt(0);
+    lds_barrier();
+    if (wave == 0) {
+      unsigned released = 0u;
+      if (lane == 0) {
+        const unsigned gsize = (nblk - (unsigned)grp + kChainBarGroups - 1) / kChainBarGroups;
+        const unsigned prev =
+            __hip_atomic_fetch_add(slot(grp), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (prev == gsize - 1) {
+          st_agent_u32(slot(grp), 0u);
+          __builtin_amdgcn_s_waitcnt(0);            // re-armed before the group counts as done
+          const unsigned done = __hip_atomic_fetch_add(slot(kChainBarGroups), 1u, __ATOMIC_RELAXED,
+                                                       __HIP_MEMORY_SCOPE_AGENT);
+          if (done == (unsigned)ngroups - 1) {
+            st_agent_u32(slot(kChainBarGroups), 0u);
+            __builtin_amdgcn_s_waitcnt(0);          // re-armed before anyone is released
+            released = 1u;
+          }
+        }
+        s_flag[WT] = released;
+      }
+      released = __shfl(released, 0, 64);
+      if (released && lane < kChainBarGroups)
+        st_agent_u32(slot(kChainBarGroups + 1 + lane), gen0 + (unsigned)l + 1u);
+    }
+    L = lins[l + 1];
+    u = plan_unit(L, b, wt, wk, lane);
+    rw = make_rsrc(L.qweight);
+    rz = make_rsrc(L.qzeros);
+    rs = make_rsrc(L.scales);
+#pragma unroll
+    for (int i = 0; i < D; ++i) {
+      load_w(f[i], rw, rz, rs, u, i);
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
 }

@@ -297,7 +297,7 @@ __global__ __launch_bounds__(64 * WT * WK) void w4a16_skinny_kernel(GemmArgs a, 
     const int t = cb * WT + (int)threadIdx.x;
     unsigned last = 0u;
     if (t < T) {                                    // tiles past N take no ticket
-      unsigned* tk = tickets + (size_t)mblk * T + t;
+      unsigned* tk = tickets + ((size_t)mblk * T + t) * kTicketStride;
       const unsigned prev = __hip_atomic_fetch_add(tk, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       if (prev == (unsigned)splits - 1) {
         __hip_atomic_store(tk, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

@@ -12,12 +12,15 @@ constexpr int kColTile = 64;       // output columns per wave (4 per lane x 16 l
 constexpr int kWorkspaceAlign = 256;
 
 // Every workspace that needs arrival counters starts with this fixed counter
-// region (one 32-bit counter per output tile); partial results follow it.
-// Because the counters sit at the same place for every shape and every
-// kernel leaves them at zero, calls of different shapes may share one
-// workspace as long as they are ordered on one stream.
+// region (one 32-bit counter per output tile, each in a 256-byte slot of its
+// own: counters that share a cache line serialise their atomics at the
+// memory side); partial results follow it.  Because the counters sit at the
+// same place for every shape and every kernel leaves them at zero, calls of
+// different shapes may share one workspace as long as they are ordered on
+// one stream.
 constexpr size_t kTicketRegion = 64 * 1024;
-constexpr size_t kMaxTickets = kTicketRegion / sizeof(unsigned);
+constexpr size_t kTicketStride = 64;            // 32-bit words between two counters
+constexpr size_t kMaxTickets = kTicketRegion / (kTicketStride * sizeof(unsigned));
 
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
@@ -78,48 +81,63 @@ hipError_t launch_lmhead_argmax(const LmheadArgs& a, const LmheadPlan& p, void* 
                                 hipStream_t stream);
 
 // ---------------------------------------------------------------- chain of linears
-constexpr unsigned kChainMagic = 0x43563457u;   // "W4VC"
-constexpr int kChainWavesPerUnit = 7;           // math waves per block (plus one control wave)
-constexpr int kChainGroupsPerWave = 2;          // 128-k groups a math wave owns per unit
+constexpr unsigned kChainMagic = 0x34435734u;   // "4WC4"
+constexpr int kChainTiles = 4;                  // 64-column tiles per block (one wave each per k-slice)
+constexpr int kChainSlices = 2;                 // k-slices per block
+constexpr int kChainThreads = 64 * kChainTiles * kChainSlices;
+constexpr int kChainMaxGroups = 24;             // 128-k groups of one unit's activation slice (LDS)
 constexpr int kChainMaxRows = 16;
 
-// Device-side header at offset 0 of a prepared chain workspace (256 bytes).
+// Device-side header at offset 0 of a prepared chain workspace (256 bytes),
+// followed by the barrier slots.
 struct ChainHeader {
   unsigned magic;
   unsigned n_linears;
-  unsigned total_units;
+  unsigned blocks;       // grid size the plan was made for (one block per CU)
   unsigned M;
-  unsigned work;         // unit dispenser (re-armed by the kernel)
-  unsigned exit_count;   // blocks that finished (re-armed by the kernel)
-  unsigned epoch;        // flags of the current launch hold epoch + 1
-  unsigned error;        // 1: a wait timed out, 2: workspace not prepared for this call
+  unsigned bar_gen;      // grid barriers completed since the workspace was prepared
+  unsigned abort;        // a launch gave up a wait: results invalid until prepared again
+  unsigned unused;
+  unsigned error;        // byte offset 28: 1 a wait timed out, 2 workspace not prepared for this call
   unsigned K0;           // width of the input rows
   unsigned N_last;       // width of the output rows
   unsigned pad0[2];
   uint64_t lin_offset;   // byte offset of the ChainLinear table
-  uint64_t unit_offset;  // byte offset of the unit -> linear table (uint16)
-  unsigned pad1[48];
+  uint64_t pad1;
+  unsigned pad2[48];
 };
 static_assert(sizeof(ChainHeader) == 256, "chain header is 256 bytes");
+
+// Grid barrier slots after the header, each 32-bit word alone in 256 bytes
+// (words that share a cache line serialise their atomics and loads at the
+// memory side): kChainBarGroups arrival counters (block b counts in group
+// b % kChainBarGroups), one counter of finished groups, and kChainBarGroups
+// copies of the generation word (block b polls copy b % kChainBarGroups)
+// each followed by a copy of the abort word.
+constexpr int kChainBarGroups = 16;
+constexpr size_t kChainSlot = 256;
+constexpr size_t kChainBarBytes = (2 * kChainBarGroups + 1) * kChainSlot;
 
 struct ChainLinear {
   const uint32_t* qweight;
   const _Float16* scales;
   const uint32_t* qzeros;
   _Float16* out;         // fp16 [16 x ldo] output (unused for the last linear)
-  float* partials;       // fp32 [splits][16][ct*64] when splits > 1
-  unsigned* tickets;     // [ct] split arrivals per tile (splits > 1)
-  unsigned* flags;       // [ct] epoch + 1 once the tile's output is written
-  int K, N, ldo, splits, ct, unit0;
+  float* partials;       // fp32 [splits][16][cb * 4 * 64] when splits > 1
+  unsigned* tickets;     // [cb * 4] split arrivals per tile (splits > 1)
+  void* unused;
+  int K, N, ldo, splits;
+  int cb;                // column blocks of 4 tiles
+  int units;             // cb * splits <= blocks: one unit per block
   float alpha;
   int pad;
 };
+static_assert(sizeof(ChainLinear) == 88, "chain linear descriptor is 88 bytes");
 
 struct ChainLayout {
   size_t bytes;          // total workspace bytes
-  size_t lin_offset, unit_offset;
-  size_t counters_offset, counters_bytes;   // flags + tickets, zeroed by prepare
-  unsigned total_units;
+  size_t lin_offset;
+  size_t counters_offset, counters_bytes;   // tickets, zeroed by prepare
 };
 
 hipError_t launch_w4a16_chain(ChainHeader* hdr, const _Float16* x, int64_t ldx, _Float16* y,
