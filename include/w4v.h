@@ -165,15 +165,19 @@ int w8a16_lmhead_argmax_verify(const void* h, int64_t ldh,
  * to fp16 exactly as a separate w4a16_gemm call would round it.
  *
  * One block per compute unit stays resident for the whole chain; the plan
- * gives every linear at most one unit (256 output columns x one K-split) per
- * block, and linears are separated by a grid barrier.
+ * gives every linear at most one unit (64, 128 or 256 output columns x one
+ * K-split) per block.  A unit of linear l waits only for the 64-column
+ * tiles of linear l-1's output that it reads (per-tile ready flags in the
+ * workspace), and a block starts streaming its next unit's weights while the
+ * current unit is reduced and published.
  *
  * w4a16_chain_prepare writes the launch plan (per-linear descriptors,
- * buffers, counters) for the current device's compute-unit count into the
+ * buffers) for the current device's compute-unit count into the
  * caller's workspace with synchronous copies; it must not run while a call
  * that uses this workspace is in flight.  The prepared workspace is then used
  * by any number of w4a16_chain calls ordered on one stream, on the same
- * device (also from a captured graph: the kernel re-arms its own counters).
+ * device (also from a captured graph: each launch leaves the buffers the
+ * next launch writes in their prepared state).
  * The linears' device arrays must stay valid and unchanged.
  *
  * linears    host array of n_linears descriptors (device pointers inside),
@@ -187,7 +191,7 @@ int w8a16_lmhead_argmax_verify(const void* h, int64_t ldh,
  *            ldy % 8 == 0; must not overlap x.
  * workspace  w4a16_chain_workspace_size(...) bytes, 256-byte aligned.  Byte
  *            offset 28 holds an error word the kernel sets (sticky until the
- *            caller clears it): 1 = a barrier wait exceeded its bound
+ *            caller clears it): 1 = a wait for another block's output exceeded its bound
  *            (results invalid; the workspace must be prepared again),
  *            2 = the workspace was not prepared for this M, K_0, N_{n-1} and
  *            device, or a previous call gave up a wait (nothing computed).

@@ -13,13 +13,14 @@ pytestmark = pytest.mark.gpu
 
 # ChainLinear (w4v_launch.h): 7 pointers, 6 ints, float, int
 _LIN = np.dtype([("qweight", "<u8"), ("scales", "<u8"), ("qzeros", "<u8"), ("out", "<u8"),
-                 ("partials", "<u8"), ("tickets", "<u8"), ("unused", "<u8"), ("K", "<i4"),
-                 ("N", "<i4"), ("ldo", "<i4"), ("splits", "<i4"), ("cb", "<i4"),
-                 ("units", "<i4"), ("alpha", "<f4"), ("pad", "<i4")])
+                 ("partials", "<u8"), ("tickets", "<u8"), ("flags", "<u8"), ("K", "<i4"),
+                 ("N", "<i4"), ("ldo", "<i4"),
+                 ("splits", "<i4"), ("cb", "<i4"), ("units", "<i4"), ("alpha", "<f4"),
+                 ("wt", "<i4")])
 
 
 def intermediates(chain):
-    """fp16 outputs of linears 0..n-2 as written in the workspace."""
+    """fp16 outputs of linears 0..n-2 as the last launch wrote them."""
     import torch
     torch.cuda.synchronize()
     ws = chain.workspace
@@ -30,8 +31,8 @@ def intermediates(chain):
     base = ws.data_ptr()
     outs = []
     for l in range(n - 1):
-        off = int(tab["out"][l]) - base
         ldo, N = int(tab["ldo"][l]), int(tab["N"][l])
+        off = int(tab["out"][l]) - base
         buf = ws[off:off + 16 * ldo * 2].view(torch.float16).view(16, ldo)
         outs.append(host(buf[:chain.m, :N]))
     return outs

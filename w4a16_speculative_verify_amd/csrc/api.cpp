@@ -94,32 +94,83 @@ int run_lmhead(const void* h, int64_t ldh, const int8_t* w, const void* scales,
   return e == hipSuccess ? W4V_OK : W4V_ERR_HIP;
 }
 
-// Split count of linear (K, N) for a grid of `blocks` blocks: as many units
-// (column blocks of 4 tiles x splits) as fit one per block, with about two
-// groups per split or more (one per k-slice) and every unit's activation
-// slice fitting in LDS.  0 when no split count fits.
-int chain_splits(int K, int N, int blocks) {
+// Unit shape of linear (K, N) for a grid of `blocks` blocks: wt 64-column
+// tiles per column block and S K-splits, with cb * S <= blocks and every
+// unit's activation slice fitting in LDS.  Among the shapes that fit, the one
+// with the least estimated time: the slowest block's weight stream (at most
+// one compute unit's share of the load bandwidth, and never faster than the
+// whole linear at the HBM rate), its activation slice, and for S > 1 the
+// round trips of the split hand-off plus the last split's read of the
+// partials.  Returns false when no shape fits.
+struct ChainShape { int wt, splits; };
+bool chain_shape(int K, int N, int blocks, ChainShape* out) {
+  constexpr double kCuBytesPerNs = 50.0;      // one CU streaming alone
+  constexpr double kHbmBytesPerNs = 7000.0;   // the whole chip
+  constexpr double kL2BytesPerNs = 100.0;     // one CU reading activations
+  constexpr double kSplitNs = 1500.0;         // partial store, ticket, partial loads
   const int G = K / w4v::kGroup;
   const int T = (N + w4v::kColTile - 1) / w4v::kColTile;
-  const int cb = (T + w4v::kChainTiles - 1) / w4v::kChainTiles;
-  const int s_min = (G + w4v::kChainMaxGroups - 1) / w4v::kChainMaxGroups;
-  const int s_max = G / w4v::kChainSlices > 1 ? G / w4v::kChainSlices : 1;
-  int s = blocks / cb;
-  if (s > s_max) s = s_max;
-  if (s < s_min) s = s_min;
-  if (s < 1 || s > G || (long)cb * s > blocks || (G + s - 1) / s > w4v::kChainMaxGroups) return 0;
-  return s;
+  const double total = (double)K * N / 2;
+  double best = 0;
+  bool found = false;
+  for (int wt = 1; wt <= 4; wt *= 2) {
+    const int cb = (T + wt - 1) / wt;
+    if (cb > blocks) continue;
+    const int s_max = blocks / cb < G ? blocks / cb : G;
+    for (int S = 1; S <= s_max; ++S) {
+      const int glen = (G + S - 1) / S;
+      if (glen > w4v::kChainMaxGroups) continue;
+      const double wbytes = (double)glen * wt * w4v::kColTile * w4v::kGroup / 2;
+      const double xbytes = (double)glen * 16 * w4v::kGroup * 2;
+      double t = wbytes / kCuBytesPerNs;
+      if (t < total / kHbmBytesPerNs) t = total / kHbmBytesPerNs;
+      t += xbytes / kL2BytesPerNs;
+      if (S > 1) t += kSplitNs + (double)S * wt * 16 * w4v::kColTile * 4 / kCuBytesPerNs;
+      if (!found || t < best) {
+        best = t;
+        *out = ChainShape{wt, S};
+        found = true;
+      }
+    }
+  }
+  return found;
 }
 
-// Checks the descriptors and lays out the workspace for a grid of `blocks`.  Host-only.
+// Workspace bytes of linear l's ready flags (one word per 64-column tile),
+// split tickets, output (16 rows; none for the last linear) and split
+// partials.
+size_t chain_flag_bytes(int N) {
+  const int T = (N + w4v::kColTile - 1) / w4v::kColTile;
+  return w4v::align_up((size_t)T * sizeof(unsigned), 256);
+}
+size_t chain_out_bytes(int N) {
+  const int T = (N + w4v::kColTile - 1) / w4v::kColTile;
+  return w4v::align_up(16 * (size_t)T * w4v::kColTile * 2, 256);
+}
+size_t chain_ticket_bytes(int N, const ChainShape& sh) {
+  const int T = (N + w4v::kColTile - 1) / w4v::kColTile;
+  const int cb = (T + sh.wt - 1) / sh.wt;
+  return sh.splits == 1 ? 0 : (size_t)cb * sh.wt * w4v::kChainSlot;
+}
+size_t chain_partial_bytes(int N, const ChainShape& sh) {
+  const int T = (N + w4v::kColTile - 1) / w4v::kColTile;
+  const int cb = (T + sh.wt - 1) / sh.wt;
+  if (sh.splits == 1) return 0;
+  return w4v::align_up((size_t)sh.splits * 16 * cb * sh.wt * w4v::kColTile * 4, 256);
+}
+
+// Checks the descriptors and lays out the workspace for a grid of `blocks`:
+// header, descriptor table, ready flags and tickets (zeroed by prepare), then
+// the intermediate outputs and split partials.  Host-only.
 int chain_layout(const w4v_chain_linear* lins, int n, int M, int blocks, w4v::ChainLayout* lay) {
   if (!lins || n < 1 || n > 65535) return W4V_ERR_INVALID_ARG;
   if (M < 1) return W4V_ERR_INVALID_ARG;
   if (M > w4v::kChainMaxRows) return W4V_ERR_UNSUPPORTED;
   if (blocks < 1) return W4V_ERR_HIP;
-  size_t off = sizeof(w4v::ChainHeader) + w4v::kChainBarBytes;
+  size_t off = sizeof(w4v::ChainHeader);
   lay->lin_offset = off;
   off += w4v::align_up((size_t)n * sizeof(w4v::ChainLinear), 256);
+  ChainShape sh{};
   for (int l = 0; l < n; ++l) {
     const w4v_chain_linear& L = lins[l];
     if (L.K <= 0 || L.N <= 0 || L.K % w4v::kGroup != 0 || L.N % 8 != 0) return W4V_ERR_INVALID_ARG;
@@ -129,24 +180,18 @@ int chain_layout(const w4v_chain_linear* lins, int n, int M, int blocks, w4v::Ch
       return W4V_ERR_ALIGNMENT;
     // buffer resources take 32-bit offsets below 2 GiB
     if ((size_t)L.K * L.N / 2 >= (1ull << 31)) return W4V_ERR_UNSUPPORTED;
-    if (chain_splits(L.K, L.N, blocks) == 0) return W4V_ERR_UNSUPPORTED;
+    if (!chain_shape(L.K, L.N, blocks, &sh)) return W4V_ERR_UNSUPPORTED;
   }
   lay->counters_offset = off;
-  size_t cnt = 0;
   for (int l = 0; l < n; ++l) {
-    const int T = (lins[l].N + w4v::kColTile - 1) / w4v::kColTile;
-    const int cb = (T + w4v::kChainTiles - 1) / w4v::kChainTiles;
-    cnt += (size_t)cb * w4v::kChainTiles * w4v::kChainSlot;   // one slot per tile's counter
+    chain_shape(lins[l].K, lins[l].N, blocks, &sh);
+    off += chain_flag_bytes(lins[l].N) + chain_ticket_bytes(lins[l].N, sh);
   }
-  lay->counters_bytes = cnt;
-  off += cnt;
+  lay->buffers_offset = off;
   for (int l = 0; l < n; ++l) {
-    const int T = (lins[l].N + w4v::kColTile - 1) / w4v::kColTile;
-    const int cb = (T + w4v::kChainTiles - 1) / w4v::kChainTiles;
-    const size_t ldo = (size_t)T * w4v::kColTile;
-    if (l < n - 1) off += w4v::align_up(16 * ldo * 2, 256);
-    const int S = chain_splits(lins[l].K, lins[l].N, blocks);
-    if (S > 1) off += w4v::align_up((size_t)S * 16 * cb * w4v::kChainTiles * w4v::kColTile * 4, 256);
+    chain_shape(lins[l].K, lins[l].N, blocks, &sh);
+    if (l < n - 1) off += chain_out_bytes(lins[l].N);
+    off += chain_partial_bytes(lins[l].N, sh);
   }
   lay->bytes = off;
   return W4V_OK;
@@ -301,39 +346,45 @@ int w4a16_chain_prepare(const w4v_chain_linear* linears, int n_linears, int M, v
   hdr->lin_offset = lay.lin_offset;
   w4v::ChainLinear* tab = reinterpret_cast<w4v::ChainLinear*>(img.data() + lay.lin_offset);
   size_t cnt_off = lay.counters_offset;
-  size_t buf_off = lay.counters_offset + lay.counters_bytes;
+  size_t buf_off = lay.buffers_offset;
   for (int l = 0; l < n_linears; ++l) {
     const w4v_chain_linear& L = linears[l];
     w4v::ChainLinear& d = tab[l];
     const int T = (L.N + w4v::kColTile - 1) / w4v::kColTile;
-    const int cb = (T + w4v::kChainTiles - 1) / w4v::kChainTiles;
-    const int S = chain_splits(L.K, L.N, blocks);
+    ChainShape sh{};
+    chain_shape(L.K, L.N, blocks, &sh);
+    const int cb = (T + sh.wt - 1) / sh.wt;
     d.qweight = reinterpret_cast<const uint32_t*>(L.qweight);
     d.scales = static_cast<const _Float16*>(L.scales);
     d.qzeros = reinterpret_cast<const uint32_t*>(L.qzeros);
     d.K = L.K;
     d.N = L.N;
+    d.wt = sh.wt;
     d.cb = cb;
-    d.splits = S;
-    d.units = cb * S;
+    d.splits = sh.splits;
+    d.units = cb * sh.splits;
     d.alpha = L.alpha;
     d.ldo = T * w4v::kColTile;
+    d.flags = reinterpret_cast<unsigned*>(base + cnt_off);
+    cnt_off += chain_flag_bytes(L.N);
     d.tickets = reinterpret_cast<unsigned*>(base + cnt_off);
-    cnt_off += (size_t)cb * w4v::kChainTiles * w4v::kChainSlot;
+    cnt_off += chain_ticket_bytes(L.N, sh);
     d.out = nullptr;
     if (l < n_linears - 1) {
       d.out = reinterpret_cast<_Float16*>(base + buf_off);
-      buf_off += w4v::align_up(16 * (size_t)d.ldo * 2, 256);
+      buf_off += chain_out_bytes(L.N);
     }
     d.partials = nullptr;
-    if (S > 1) {
+    if (sh.splits > 1) {
       d.partials = reinterpret_cast<float*>(base + buf_off);
-      buf_off += w4v::align_up((size_t)S * 16 * cb * w4v::kChainTiles * w4v::kColTile * 4, 256);
+      buf_off += chain_partial_bytes(L.N, sh);
     }
   }
   if (hipMemcpy(workspace, img.data(), img.size(), hipMemcpyHostToDevice) != hipSuccess)
     return W4V_ERR_HIP;
-  if (hipMemset(base + lay.counters_offset, 0, lay.counters_bytes) != hipSuccess) return W4V_ERR_HIP;
+  if (hipMemset(base + lay.counters_offset, 0, lay.buffers_offset - lay.counters_offset) !=
+      hipSuccess)
+    return W4V_ERR_HIP;
   if (hipDeviceSynchronize() != hipSuccess) return W4V_ERR_HIP;
   return W4V_OK;
 }

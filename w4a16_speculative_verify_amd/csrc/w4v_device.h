@@ -178,6 +178,12 @@ template <int Aux = 0>
 __device__ __forceinline__ u32x4 ld_x4(rsrc_t r, uint32_t off) {
   return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, Aux);
 }
+// The same with a wave-uniform byte offset in the scalar operand (added to
+// the per-lane offset before the range check).
+template <int Aux = 0>
+__device__ __forceinline__ u32x4 ld_x4s(rsrc_t r, uint32_t off, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, off, soff, Aux);
+}
 __device__ __forceinline__ u32x2 ld_x2(rsrc_t r, uint32_t off) {
   return __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
 }

@@ -81,23 +81,22 @@ hipError_t launch_lmhead_argmax(const LmheadArgs& a, const LmheadPlan& p, void* 
                                 hipStream_t stream);
 
 // ---------------------------------------------------------------- chain of linears
-constexpr unsigned kChainMagic = 0x34435734u;   // "4WC4"
-constexpr int kChainTiles = 4;                  // 64-column tiles per block (one wave each per k-slice)
-constexpr int kChainSlices = 2;                 // k-slices per block
-constexpr int kChainThreads = 64 * kChainTiles * kChainSlices;
+constexpr unsigned kChainMagic = 0x37435734u;   // "4WC7"
+constexpr int kChainComputeWaves = 4;           // tiles x k-slices of a unit
+constexpr int kChainThreads = 64 * (kChainComputeWaves + 1);   // + one control wave
 constexpr int kChainMaxGroups = 24;             // 128-k groups of one unit's activation slice (LDS)
 constexpr int kChainMaxRows = 16;
+constexpr size_t kChainSlot = 256;              // bytes per ticket (one cache line or more)
 
-// Device-side header at offset 0 of a prepared chain workspace (256 bytes),
-// followed by the barrier slots.
+// Device-side header at offset 0 of a prepared chain workspace (256 bytes).
 struct ChainHeader {
   unsigned magic;
   unsigned n_linears;
   unsigned blocks;       // grid size the plan was made for (one block per CU)
   unsigned M;
-  unsigned bar_gen;      // grid barriers completed since the workspace was prepared
+  unsigned epoch;        // launches completed: launch e raises flags to e + 1
   unsigned abort;        // a launch gave up a wait: results invalid until prepared again
-  unsigned unused;
+  unsigned exit_count;   // blocks that finished the current launch (re-armed by the last)
   unsigned error;        // byte offset 28: 1 a wait timed out, 2 workspace not prepared for this call
   unsigned K0;           // width of the input rows
   unsigned N_last;       // width of the output rows
@@ -108,36 +107,27 @@ struct ChainHeader {
 };
 static_assert(sizeof(ChainHeader) == 256, "chain header is 256 bytes");
 
-// Grid barrier slots after the header, each 32-bit word alone in 256 bytes
-// (words that share a cache line serialise their atomics and loads at the
-// memory side): kChainBarGroups arrival counters (block b counts in group
-// b % kChainBarGroups), one counter of finished groups, and kChainBarGroups
-// copies of the generation word (block b polls copy b % kChainBarGroups)
-// each followed by a copy of the abort word.
-constexpr int kChainBarGroups = 16;
-constexpr size_t kChainSlot = 256;
-constexpr size_t kChainBarBytes = (2 * kChainBarGroups + 1) * kChainSlot;
-
 struct ChainLinear {
   const uint32_t* qweight;
   const _Float16* scales;
   const uint32_t* qzeros;
-  _Float16* out;         // fp16 [16 x ldo] output (unused for the last linear)
-  float* partials;       // fp32 [splits][16][cb * 4 * 64] when splits > 1
-  unsigned* tickets;     // [cb * 4] split arrivals per tile (splits > 1)
-  void* unused;
+  _Float16* out;         // fp16 [16][ldo] (NULL for the last linear)
+  float* partials;       // fp32 [splits][16][cb * wt * 64] when splits > 1
+  unsigned* tickets;     // [cb * wt] split arrivals per tile, one 256-byte slot each
+  unsigned* flags;       // [ceil(N / 64)] tile ready flags (epoch + 1 once written)
   int K, N, ldo, splits;
-  int cb;                // column blocks of 4 tiles
+  int cb;                // column blocks of wt tiles
   int units;             // cb * splits <= blocks: one unit per block
   float alpha;
-  int pad;
+  int wt;                // 64-column tiles per block (1, 2 or 4); 4 / wt k-slices
 };
 static_assert(sizeof(ChainLinear) == 88, "chain linear descriptor is 88 bytes");
 
 struct ChainLayout {
   size_t bytes;          // total workspace bytes
   size_t lin_offset;
-  size_t counters_offset, counters_bytes;   // tickets, zeroed by prepare
+  size_t counters_offset;   // tickets and ready flags, zeroed by prepare
+  size_t buffers_offset;    // outputs and partials
 };
 
 hipError_t launch_w4a16_chain(ChainHeader* hdr, const _Float16* x, int64_t ldx, _Float16* y,
