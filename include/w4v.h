@@ -70,16 +70,29 @@ int w4v_abi_version(void);
  *          y must not overlap x.
  * Sizes    M >= 0 (M == 0 or N == 0: nothing to do, W4V_OK), K > 0,
  *          N % 8 == 0, K % group_size == 0; group_size must be 128
- *          (W4V_ERR_UNSUPPORTED otherwise).  For M <= 32 the packed weights
+ *          (W4V_ERR_UNSUPPORTED otherwise).  For M < 512 the packed weights
  *          (K*N/2 bytes), the scales and the rows of x (M*ldx*2 bytes) must
  *          each stay below 2 GiB (W4V_ERR_UNSUPPORTED otherwise).
  * alpha    epilogue scale applied to the fp32 accumulator before the single
  *          round-to-nearest-even to fp16.
+ * Paths    M <= 32: weights dequantised exactly in registers, group scale
+ *          applied to the fp32 group sum (split-K across blocks).
+ *          33 <= M < 512: the same arithmetic in an LDS-tiled MFMA kernel.
+ *          M >= 512 (prefill shapes, bound by the matrix cores): the weights
+ *          are first expanded to fp16 by this library's kernel,
+ *          w = fp16_rne(float(s) * (q - z)) (one rounding; the fp32 product is
+ *          exact), into the workspace, then multiplied by a plain fp16 GEMM of
+ *          the vendor library (fp32 accumulation, same alpha and output
+ *          rounding).  If the library offers no plan for the shape, the
+ *          LDS-tiled kernel computes the product instead.
  * workspace  device memory of at least w4a16_gemm_workspace_size(M, N, K,
  *          group_size) bytes (may be NULL when that size is 0), 256-byte
- *          aligned, zeroed once by the caller.  Holds fp32 split-K partial
- *          sums and arrival counters; the result does not depend on the
- *          order in which partial sums arrive.
+ *          aligned, zeroed once by the caller.  Its first 64 KiB hold arrival
+ *          counters (left at zero by every call), then fp32 split-K partial
+ *          sums (M <= 32) or, for M >= 512, the fp16 expanded weights (2*K*N
+ *          bytes) and the library GEMM's scratch; the result does not depend
+ *          on the order in which partial sums arrive.  One workspace sized for
+ *          the largest call serves calls of every shape ordered on one stream.
  * ---------------------------------------------------------------------- */
 size_t w4a16_gemm_workspace_size(int M, int N, int K, int group_size);
 

@@ -165,3 +165,65 @@ def test_large_m_sampled_columns(lib, m, shape):
     ref = og.w4a16_gemm_columns(x, lin.qweight, lin.scales, lin.qzeros, cols)
     check_gemm(y[:, cols], ref, f"m={m} {k}->{n}")
     assert np.all(np.isfinite(y.astype(np.float32)))
+
+
+# ---- M >= 512: weights dequantised to fp16 by the library's kernel, then a plain fp16 GEMM
+@pytest.mark.parametrize("m,k,n", [
+    (511, 384, 136),           # last row count of the tiled kernel
+    (512, 384, 136),           # first row count of the dequantise + GEMM path, ragged N
+    (600, 1280, 1032),
+    (1000, 128, 8),            # one group, narrowest N
+])
+def test_library_path_shapes(lib, m, k, n):
+    log(f"gemm m={m} k={k} n={n}")
+    rng = np.random.default_rng(3000 + m + k + n)
+    lin = gen.qlinear(rng, k, n)
+    x = gen.activations(rng, m, k)
+    y = run_gemm(lib, x, lin, alpha=0.75)
+    rel, mx = check_gemm(y, og.w4a16_gemm(x, lin.qweight, lin.scales, lin.qzeros, alpha=0.75),
+                         f"{m}x{k}x{n}")
+    log(f"  rel-L2 {rel:.2e} max/rms {mx:.2e}")
+
+
+@pytest.mark.parametrize("enc", range(3))
+def test_library_path_identity_bit_exact(lib, enc):
+    """Identity weights stay exact through the fp16 expansion (q - z in {0, 1}, scale 1 or 0.5 x 2)."""
+    n, m = 512, 640
+    eye = np.eye(n, dtype=np.int64)
+    g = n // 128
+    q, z, s = [
+        (eye, np.zeros((g, n), np.int64), np.ones((g, n), np.float16)),
+        (8 + eye, np.full((g, n), 8, np.int64), np.ones((g, n), np.float16)),
+        (7 + 2 * eye, np.full((g, n), 7, np.int64), np.full((g, n), 0.5, np.float16)),
+    ][enc]
+    lin = gen.QLinear(gen.pack_int4_along_k(q), s, gen.pack_int4_along_n(z), n, n)
+    x = gen.activations(np.random.default_rng(enc), m, n)
+    y = run_gemm(lib, x, lin)
+    assert np.array_equal(y.view(np.uint16), x.view(np.uint16))
+
+
+def test_library_path_strided_and_shared_workspace(lib):
+    """Row-strided x and y at M = 700, then M = 16 split-K calls on the same workspace: the
+    counter prefix the split-K path relies on is left at zero by the M >= 512 path."""
+    import torch
+    rng = np.random.default_rng(31)
+    k, n, m = 1024, 520, 700
+    lin = gen.qlinear(rng, k, n)
+    wide = gen.activations(rng, m, 1536)
+    need = max(lib.gemm_workspace_size(m, n, k), lib.gemm_workspace_size(16, 2560, 9728))
+    ws = lib.new_workspace(need)
+    out_wide = torch.full((m, 800), 7.0, dtype=torch.float16, device="cuda")
+    out = out_wide[:, 96:96 + n]               # 192 bytes in: 16-byte aligned
+    lib.w4a16_gemm(dev(wide)[:, :k], dev(lin.qweight), dev(lin.scales), dev(lin.qzeros), out=out,
+                   workspace=ws)
+    torch.cuda.synchronize()
+    full = host(out_wide)
+    check_gemm(full[:, 96:96 + n], og.w4a16_gemm(wide[:, :k], lin.qweight, lin.scales, lin.qzeros),
+               "strided m=700")
+    assert np.all(full[:, :96] == 7.0) and np.all(full[:, 96 + n:] == 7.0)
+    assert int(torch.count_nonzero(ws[:65536])) == 0
+    lin2 = gen.qlinear(rng, 9728, 2560)
+    for _ in range(2):
+        x2 = gen.activations(rng, 16, 9728)
+        y2 = run_gemm(lib, x2, lin2, ws=ws)
+        check_gemm(y2, og.w4a16_gemm(x2, lin2.qweight, lin2.scales, lin2.qzeros), "split-K after")

@@ -13,7 +13,10 @@ INCLUDE = os.path.join(ROOT, "include")
 OBJDIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libw4v.so")
 
-SOURCES = ["w4a16_skinny.hip", "w4a16_tiled.hip", "w4a16_chain.hip", "w8a16_lmhead.hip", "greedy_verify.hip", "api.cpp"]
+SOURCES = ["w4a16_skinny.hip", "w4a16_tiled.hip", "w4a16_dequant.hip", "w4a16_chain.hip",
+           "w8a16_lmhead.hip", "greedy_verify.hip", "lib_gemm.cpp", "api.cpp"]
+# the vendor GEMM library behind the prefill-shaped linear's plain fp16 product
+LIBS = ["-L/opt/rocm/lib", "-lhipblaslt", "-Wl,-rpath,/opt/rocm/lib"]
 
 # gfx950 only.  Packed-fp32 instructions are switched off for every HIP
 # translation unit (the host pass reports the feature as unknown; harmless).
@@ -56,7 +59,7 @@ def build(verbose: bool = False) -> str:
     with ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as pool:
         objs = list(pool.map(lambda s: _compile(s, hipcc, verbose), SOURCES))
     tmp = LIB + ".tmp"
-    cmd = [hipcc, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
+    cmd = [hipcc, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, *LIBS, "-o", tmp]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"link failed:\n{res.stdout}\n{res.stderr}")

@@ -229,10 +229,19 @@ const char* w4v_status_string(int status) {
 
 int w4v_abi_version(void) { return W4V_ABI_VERSION; }
 
+// Workspace of the library path (M >= kLibMinRows): the fixed counter prefix
+// is left alone (so one workspace still serves calls of every shape), then
+// the transposed fp16 weights, then the library GEMM's scratch.
+static size_t lib_weights_bytes(int N, int K) { return w4v::align_up((size_t)N * K * 2, 256); }
+static size_t lib_workspace_bytes(int N, int K) {
+  return w4v::kTicketRegion + lib_weights_bytes(N, K) + w4v::kLibWorkspace;
+}
+
 size_t w4a16_gemm_workspace_size(int M, int N, int K, int group_size) {
   if (M <= 0 || N <= 0 || K <= 0 || group_size != w4v::kGroup || K % group_size != 0 ||
       N % 8 != 0)
     return 0;
+  if (M >= w4v::kLibMinRows) return lib_workspace_bytes(N, K);
   if (M >= w4v::kTiledMinRows) return 0;
   return w4v::plan_w4a16(M, N, K, kPlanCUs).workspace_bytes();
 }
@@ -242,16 +251,21 @@ int w4a16_gemm(const void* x, int64_t ldx, const int32_t* qweight, const void* s
                float alpha, void* workspace, size_t workspace_bytes, void* stream) {
   int st = gemm_check(x, ldx, qweight, scales, qzeros, y, ldy, M, N, K, group_size);
   if (st != W4V_OK || M == 0 || N == 0) return st;
+  const bool lib = M >= w4v::kLibMinRows;
   const bool tiled = M >= w4v::kTiledMinRows;
   if (tiled && (M + 127) / 128 > kMaxGridYZ) return W4V_ERR_UNSUPPORTED;
+  // buffer resources take 32-bit offsets below 2 GiB
+  const bool big = (size_t)K * N / 2 >= (1ull << 31) || (size_t)M * ldx * 2 >= (1ull << 31) ||
+                   (size_t)K / 128 * N * 2 >= (1ull << 31);
+  if (tiled && !lib && big) return W4V_ERR_UNSUPPORTED;
+  if (lib) {
+    st = workspace_check(lib_workspace_bytes(N, K), workspace, workspace_bytes);
+    if (st != W4V_OK) return st;
+  }
   w4v::GemmPlan p{};
   if (!tiled) {
     p = w4v::plan_w4a16(M, N, K, kPlanCUs);
-    // buffer resources take 32-bit offsets below 2 GiB
-    if ((size_t)K * N / 2 >= (1ull << 31) || (size_t)M * ldx * 2 >= (1ull << 31) ||
-        (size_t)K / 128 * N * 2 >= (1ull << 31) || p.mblocks > kMaxGridYZ ||
-        p.splits > kMaxGridYZ)
-      return W4V_ERR_UNSUPPORTED;
+    if (big || p.mblocks > kMaxGridYZ || p.splits > kMaxGridYZ) return W4V_ERR_UNSUPPORTED;
     st = workspace_check(p.workspace_bytes(), workspace, workspace_bytes);
     if (st != W4V_OK) return st;
   }
@@ -267,8 +281,21 @@ int w4a16_gemm(const void* x, int64_t ldx, const int32_t* qweight, const void* s
   a.N = N;
   a.K = K;
   a.alpha = alpha;
-  hipError_t e = tiled ? w4v::launch_w4a16_tiled(a, static_cast<hipStream_t>(stream))
-                       : w4v::launch_w4a16_skinny(a, p, workspace, static_cast<hipStream_t>(stream));
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (lib) {
+    // weights to fp16 (our kernel), then the plain GEMM; if the library has
+    // no plan for the shape (or the weights exceed the tiled kernel's range
+    // anyway), the LDS-tiled kernel computes the same product
+    char* base = static_cast<char*>(workspace) + w4v::kTicketRegion;
+    _Float16* wt = reinterpret_cast<_Float16*>(base);
+    hipError_t e = w4v::launch_dequant_w4_f16t(a.qweight, a.scales, a.qzeros, K, N, wt, s);
+    if (e != hipSuccess) return W4V_ERR_HIP;
+    if (w4v::lib_gemm_f16_tn(a.x, ldx, wt, a.y, ldy, M, N, K, alpha,
+                             base + lib_weights_bytes(N, K), w4v::kLibWorkspace, s))
+      return W4V_OK;
+    if (big) return W4V_ERR_HIP;
+  }
+  hipError_t e = tiled ? w4v::launch_w4a16_tiled(a, s) : w4v::launch_w4a16_skinny(a, p, workspace, s);
   return e == hipSuccess ? W4V_OK : W4V_ERR_HIP;
 }
 

@@ -14,8 +14,9 @@
 //     memory (4 columns x 8 k per 128-bit load, the lane layout of the MFMA B
 //     operand), dequantises them in registers exactly (fp16 q - z), and the
 //     group's fp16 scale multiplies the fp32 sum of the group once.
-//   The next group's weights and activations are requested before the
-//   current group's MFMAs run.
+//   Weights run two groups ahead in a three-deep register ring, the next
+//   group's activations are requested before the current group's MFMAs; the
+//   per-group barrier orders LDS only, so loads stay in flight across it.
 #include "w4v_device.h"
 #include "w4v_launch.h"
 
@@ -27,6 +28,7 @@ constexpr int kThreads = 256;
 constexpr int BM = 128, BN = 128, BK = 128;
 constexpr int kRowBytes = BK * 2 + 16;            // padded LDS row of A
 constexpr int kRowWords = kRowBytes / 4;
+constexpr int DB = 3;                             // weight groups in flight per lane
 
 struct BFrag {
   u32x4 w[4];       // 4 quads of packed rows, 4 columns each
@@ -34,13 +36,21 @@ struct BFrag {
   u32x2 s;          // 4 fp16 scales
 };
 
-__device__ __forceinline__ void load_b(BFrag& f, const GemmArgs& a, int g, int col, int kb) {
-  const int N = a.N;
+// Lane byte offsets of group 0's loads and the per-group strides.
+struct BLanes {
+  uint32_t w, wq, gw, z, gz, s, gs;
+};
+
+// Group g's packed words, zero-point word and scales; a group past the last
+// one reads zeros without touching memory (offset pushed past the resource).
+__device__ __forceinline__ void load_b(BFrag& f, const rsrc_t& rw, const rsrc_t& rz,
+                                       const rsrc_t& rs, const BLanes& o, int g, int G) {
+  const uint32_t gg = (uint32_t)(g < G ? g : 0);
+  const uint32_t skip = g < G ? 0u : kNoLoad;
 #pragma unroll
-  for (int it = 0; it < 4; ++it)
-    f.w[it] = *reinterpret_cast<const u32x4*>(a.qweight + (size_t)(g * 16 + it * 4 + kb) * N + col);
-  f.zw = a.qzeros[(size_t)g * (N >> 3) + (col >> 3)];
-  f.s = *reinterpret_cast<const u32x2*>(a.scales + (size_t)g * N + col);
+  for (int it = 0; it < 4; ++it) f.w[it] = ld_x4<kNT>(rw, (o.w + it * o.wq + gg * o.gw) | skip);
+  f.zw = ld_x1(rz, (o.z + gg * o.gz) | skip);
+  f.s = ld_x2(rs, (o.s + gg * o.gs) | skip);
 }
 
 // A tile loads: thread t moves 8 consecutive k (16 bytes) of rows t/16 + 16 j.
@@ -48,24 +58,19 @@ struct AFrag {
   u32x4 v[8];
 };
 
-__device__ __forceinline__ void load_a(AFrag& f, const GemmArgs& a, int m0, int g, int t) {
-  const int chunk = t & 15;
+__device__ __forceinline__ void load_a(AFrag& f, const rsrc_t& rx, const uint32_t (&oa)[8], int g,
+                                       int G) {
+  const uint32_t skip = g < G ? (uint32_t)g * BK * 2 : kNoLoad;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int m = m0 + (t >> 4) + 16 * j;
-    const int mm = m < a.M ? m : a.M - 1;    // rows past M read a valid row, zeroed on store
-    f.v[j] = *reinterpret_cast<const u32x4*>(a.x + (size_t)mm * a.ldx + g * BK + chunk * 8);
-  }
+  for (int j = 0; j < 8; ++j) f.v[j] = ld_x4(rx, oa[j] + skip);
 }
 
-__device__ __forceinline__ void store_a(uint32_t* lds, const AFrag& f, const GemmArgs& a, int m0,
-                                        int t) {
+__device__ __forceinline__ void store_a(uint32_t* lds, const AFrag& f, int rows_ok, int t) {
   const int chunk = t & 15;
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     const int r = (t >> 4) + 16 * j;
-    const bool ok = m0 + r < a.M;
-    const f16x8 p = permute_for_int4(ok ? f.v[j] : u32x4{0u, 0u, 0u, 0u});
+    const f16x8 p = permute_for_int4(r < rows_ok ? f.v[j] : u32x4{0u, 0u, 0u, 0u});
     *reinterpret_cast<u32x4*>(lds + r * kRowWords + chunk * 4) = __builtin_bit_cast(u32x4, p);
   }
 }
@@ -81,6 +86,7 @@ __global__ __launch_bounds__(kThreads) void w4a16_tiled_kernel(GemmArgs a) {
   const int m0 = blockIdx.y * BM;
   const int n0 = blockIdx.x * BN;
   const int G = a.K / BK;
+  const int rows_ok = a.M - m0;                     // rows of this tile that exist
 
   const int col_raw = n0 + wn * 64 + 4 * (lane & 15);
   const bool colok = col_raw < a.N;
@@ -88,83 +94,111 @@ __global__ __launch_bounds__(kThreads) void w4a16_tiled_kernel(GemmArgs a) {
   const int zshift = (col & 4) * 4;
   const uint32_t magic = in_vgpr(0x64006400u);
 
+  const rsrc_t rw = make_rsrc(a.qweight), rz = make_rsrc(a.qzeros), rs = make_rsrc(a.scales);
+  const rsrc_t rx = make_rsrc(a.x);
+  const uint32_t N = (uint32_t)a.N;
+  BLanes ob;
+  ob.w = ((uint32_t)kb * N + col) * 4;
+  ob.wq = 16 * N;
+  ob.gw = 64 * N;
+  ob.z = (uint32_t)(col >> 3) * 4;
+  ob.gz = (N >> 3) * 4;
+  ob.s = (uint32_t)col * 2;
+  ob.gs = N * 2;
+  uint32_t oa[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int m = m0 + (t >> 4) + 16 * j;
+    const int mm = m < a.M ? m : a.M - 1;           // rows past M read a valid row, zeroed on store
+    oa[j] = ((uint32_t)mm * (uint32_t)a.ldx + (t & 15) * 8) * 2;
+  }
+
   f32x4 acc[4][4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int c = 0; c < 4; ++c) acc[i][c] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  // prologue in the loop's order: weights of groups 0 .. DB-1, then A of group 0
+  BFrag bf[DB];
+#pragma unroll
+  for (int i = 0; i < DB; ++i) {
+    load_b(bf[i], rw, rz, rs, ob, i, G);
+    __builtin_amdgcn_sched_barrier(0);
+  }
   AFrag af;
-  BFrag bf, bn;
-  load_a(af, a, m0, 0, t);
-  load_b(bf, a, 0, col, kb);
-  store_a(As[0], af, a, m0, t);
-  __syncthreads();
+  load_a(af, rx, oa, 0, G);
+  store_a(As[0], af, rows_ok, t);
+  lds_barrier();
 
-  for (int g = 0; g < G; ++g) {
-    const int buf = g & 1;
-    const bool more = g + 1 < G;
-    if (more) {
-      load_a(af, a, m0, g + 1, t);
-      load_b(bn, a, g + 1, col, kb);
-    }
-    ZeroPair zz[4];
-    {
-      const uint32_t zw = bf.zw >> zshift;
+  // steps padded to a multiple of DB: a padding step loads and computes
+  // nothing, so no load sits under a branch
+  const int gsteps = (G + DB - 1) / DB * DB;
+  for (int g0 = 0; g0 < gsteps; g0 += DB) {
 #pragma unroll
-      for (int c = 0; c < 4; ++c) zz[c] = zero_pair((zw >> (4 * c)) & 0xFu);
-    }
-    f32x4 tmp[4][4];
+    for (int i = 0; i < DB; ++i) {
+      const int g = g0 + i;
+      // the next group's activations, staged into the other LDS buffer below
+      load_a(af, rx, oa, g + 1, G);
+      if (g < G) {                                  // block-uniform
+        ZeroPair zz[4];
+        {
+          const uint32_t zw = bf[i].zw >> zshift;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+          for (int c = 0; c < 4; ++c) zz[c] = zero_pair((zw >> (4 * c)) & 0xFu);
+        }
+        f32x4 tmp[4][4];
 #pragma unroll
-      for (int c = 0; c < 4; ++c) tmp[i][c] = f32x4{0.f, 0.f, 0.f, 0.f};
-    const uint32_t* as = As[buf];
+        for (int r = 0; r < 4; ++r)
 #pragma unroll
-    for (int it = 0; it < 4; ++it) {
-      f16x8 av[4];
+          for (int c = 0; c < 4; ++c) tmp[r][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+        const uint32_t* as = As[g & 1];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = wm * 64 + i * 16 + (lane & 15);
-        av[i] = __builtin_bit_cast(
-            f16x8, *reinterpret_cast<const u32x4*>(as + r * kRowWords + it * 16 + kb * 4));
+        for (int it = 0; it < 4; ++it) {
+          f16x8 av[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int row = wm * 64 + r * 16 + (lane & 15);
+            av[r] = __builtin_bit_cast(
+                f16x8, *reinterpret_cast<const u32x4*>(as + row * kRowWords + it * 16 + kb * 4));
+          }
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            const f16x8 bv = dequant_int4_word(bf[i].w[it][c], zz[c], magic);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) tmp[r][c] = mfma16x16x32(av[r], bv, tmp[r][c]);
+          }
+        }
+        // copy the vector elements to scalars before the bit casts: a bit
+        // cast of an ext-vector element expression reads element 0 with
+        // this compiler
+        const uint32_t s_lo = bf[i].s.x, s_hi = bf[i].s.y;
+        const f16x2 s01 = __builtin_bit_cast(f16x2, s_lo);
+        const f16x2 s23 = __builtin_bit_cast(f16x2, s_hi);
+        const float sc[4] = {(float)s01.x, (float)s01.y, (float)s23.x, (float)s23.y};
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+          for (int c = 0; c < 4; ++c)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[r][c][e] = __builtin_fmaf(sc[c], tmp[r][c][e], acc[r][c][e]);
       }
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const f16x8 b = dequant_int4_word(bf.w[it][c], zz[c], magic);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) tmp[i][c] = mfma16x16x32(av[i], b, tmp[i][c]);
-      }
+      load_b(bf[i], rw, rz, rs, ob, g + DB, G);
+      store_a(As[(g + 1) & 1], af, rows_ok, t);
+      lds_barrier();
     }
-    {
-      const uint32_t s_lo = bf.s.x, s_hi = bf.s.y;
-      const f16x2 s01 = __builtin_bit_cast(f16x2, s_lo);
-      const f16x2 s23 = __builtin_bit_cast(f16x2, s_hi);
-      const float sc[4] = {(float)s01.x, (float)s01.y, (float)s23.x, (float)s23.y};
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int c = 0; c < 4; ++c)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) acc[i][c][r] = __builtin_fmaf(sc[c], tmp[i][c][r], acc[i][c][r]);
-    }
-    if (more) {
-      store_a(As[buf ^ 1], af, a, m0, t);
-      bf = bn;
-    }
-    __syncthreads();
   }
 
-  // epilogue: lane holds rows 4*(l/16)+r of each m-tile, columns col..col+3
+  // epilogue: lane holds rows 4*(l/16)+e of each m-tile, columns col..col+3
   if (!colok) return;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int r = 0; r < 4; ++r)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int m = m0 + wm * 64 + i * 16 + 4 * kb + r;
+    for (int e = 0; e < 4; ++e) {
+      const int m = m0 + wm * 64 + r * 16 + 4 * kb + e;
       if (m < a.M) {
-        const f16x2 lo = {(_Float16)(a.alpha * acc[i][0][r]), (_Float16)(a.alpha * acc[i][1][r])};
-        const f16x2 hi = {(_Float16)(a.alpha * acc[i][2][r]), (_Float16)(a.alpha * acc[i][3][r])};
+        const f16x2 lo = {(_Float16)(a.alpha * acc[r][0][e]), (_Float16)(a.alpha * acc[r][1][e])};
+        const f16x2 hi = {(_Float16)(a.alpha * acc[r][2][e]), (_Float16)(a.alpha * acc[r][3][e])};
         const u32x2 v = {__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
         *reinterpret_cast<u32x2*>(a.y + (size_t)m * a.ldy + col_raw) = v;
       }

@@ -54,6 +54,19 @@ hipError_t launch_w4a16_skinny(const GemmArgs& a, const GemmPlan& p, void* works
 hipError_t launch_w4a16_tiled(const GemmArgs& a, hipStream_t stream);
 constexpr int kTiledMinRows = 33;
 
+// From this many rows on: weights dequantised to a transposed fp16 copy in the
+// workspace, then a plain fp16 GEMM from the vendor library.
+constexpr int kLibMinRows = 512;
+constexpr size_t kLibWorkspace = 64ull << 20;   // the library GEMM's own scratch
+hipError_t launch_dequant_w4_f16t(const uint32_t* qweight, const _Float16* scales,
+                                  const uint32_t* qzeros, int K, int N, _Float16* wt,
+                                  hipStream_t stream);
+// y = alpha * x @ wt^T through the library (wt: fp16 [N x K]); false if the
+// library has no plan for the shape or reports an error before launching.
+bool lib_gemm_f16_tn(const _Float16* x, int64_t ldx, const _Float16* wt, _Float16* y, int64_t ldy,
+                     int M, int N, int K, float alpha, void* scratch, size_t scratch_bytes,
+                     hipStream_t stream);
+
 // ---------------------------------------------------------------- lm_head
 struct LmheadArgs {
   const _Float16* h; int64_t ldh;
