@@ -87,12 +87,14 @@ int w4v_abi_version(void);
  *          LDS-tiled kernel computes the product instead.
  * workspace  device memory of at least w4a16_gemm_workspace_size(M, N, K,
  *          group_size) bytes (may be NULL when that size is 0), 256-byte
- *          aligned, zeroed once by the caller.  Its first 64 KiB hold arrival
- *          counters (left at zero by every call), then fp32 split-K partial
- *          sums (M <= 32) or, for M >= 512, the fp16 expanded weights (2*K*N
- *          bytes) and the library GEMM's scratch; the result does not depend
- *          on the order in which partial sums arrive.  One workspace sized for
- *          the largest call serves calls of every shape ordered on one stream.
+ *          aligned, zeroed once by the caller.  Its first 64 KiB hold the
+ *          split-K arrival counters (every call leaves them at zero), the next
+ *          4 MiB at most the fp32 split-K partial sums (M <= 32); for M >= 512
+ *          the fp16 expanded weights (2*K*N bytes) and the library GEMM's
+ *          scratch come after those 4 MiB.  The partials are added in split
+ *          order, so the result does not depend on the order in which they
+ *          arrive.  One workspace sized for the
+ *          largest call serves calls of every shape ordered on one stream.
  * ---------------------------------------------------------------------- */
 size_t w4a16_gemm_workspace_size(int M, int N, int K, int group_size);
 

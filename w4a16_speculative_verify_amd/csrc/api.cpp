@@ -229,12 +229,14 @@ const char* w4v_status_string(int status) {
 
 int w4v_abi_version(void) { return W4V_ABI_VERSION; }
 
-// Workspace of the library path (M >= kLibMinRows): the fixed counter prefix
-// is left alone (so one workspace still serves calls of every shape), then
-// the transposed fp16 weights, then the library GEMM's scratch.
+// Workspace of the library path (M >= kLibMinRows): the counter prefix and
+// the split-K partials region are left alone (so one workspace still serves
+// calls of every shape), then the transposed fp16 weights, then the library
+// GEMM's scratch.
+static size_t lib_offset() { return w4v::kTicketRegion + w4v::kPartialRegion; }
 static size_t lib_weights_bytes(int N, int K) { return w4v::align_up((size_t)N * K * 2, 256); }
 static size_t lib_workspace_bytes(int N, int K) {
-  return w4v::kTicketRegion + lib_weights_bytes(N, K) + w4v::kLibWorkspace;
+  return lib_offset() + lib_weights_bytes(N, K) + w4v::kLibWorkspace;
 }
 
 size_t w4a16_gemm_workspace_size(int M, int N, int K, int group_size) {
@@ -265,7 +267,9 @@ int w4a16_gemm(const void* x, int64_t ldx, const int32_t* qweight, const void* s
   w4v::GemmPlan p{};
   if (!tiled) {
     p = w4v::plan_w4a16(M, N, K, kPlanCUs);
-    if (big || p.mblocks > kMaxGridYZ || p.splits > kMaxGridYZ) return W4V_ERR_UNSUPPORTED;
+    if (big || p.mblocks > kMaxGridYZ || p.splits > kMaxGridYZ ||
+        p.partial_bytes > w4v::kPartialRegion)
+      return W4V_ERR_UNSUPPORTED;
     st = workspace_check(p.workspace_bytes(), workspace, workspace_bytes);
     if (st != W4V_OK) return st;
   }
@@ -286,7 +290,7 @@ int w4a16_gemm(const void* x, int64_t ldx, const int32_t* qweight, const void* s
     // weights to fp16 (our kernel), then the plain GEMM; if the library has
     // no plan for the shape (or the weights exceed the tiled kernel's range
     // anyway), the LDS-tiled kernel computes the same product
-    char* base = static_cast<char*>(workspace) + w4v::kTicketRegion;
+    char* base = static_cast<char*>(workspace) + lib_offset();
     _Float16* wt = reinterpret_cast<_Float16*>(base);
     hipError_t e = w4v::launch_dequant_w4_f16t(a.qweight, a.scales, a.qzeros, K, N, wt, s);
     if (e != hipSuccess) return W4V_ERR_HIP;
