@@ -13,6 +13,9 @@ Sources (organisers' page "Efficient LLM Challenge Results", adaptfm.gitlab.io):
                 size 128 and an untied lm_head quantised to 8 bits; the
                 runner-up pads drafts to K=20 with -1 sentinels, and a padded
                 position is accepted only if it equals the target's greedy token.
+                Table 3 and the paragraph on n-gram drafting: the prompt-
+                lookup drafter copies spans from the prompt, no auxiliary
+                model, fixed K (23 for the team that used it).
   section 5  -- W4A16 (group size 128), W8A16 lm_head.
 
 Modules:
@@ -21,10 +24,12 @@ Modules:
   lmhead  -- 8-bit lm_head logits, argmax with tie-break, top-2 margin
   verify  -- greedy prefix acceptance with sentinels, verified-token count
   step    -- the free-running verify step (chain of linears, lm_head, verify)
+  ngram   -- prompt-lookup drafting and appending the accepted tokens
 
 Every function is pinned by a ``-m "not gpu"`` test (pack/unpack round trips,
 hand-built words, identity and one-hot weights, closed forms, exact-rational
-brute force on tiny shapes, exhaustive enumeration for the verify).  No
+brute force on tiny shapes, exhaustive enumeration for the verify and the
+drafter).  No
 function here is "parity unpinned".
 """
-from . import quant, gemm, lmhead, verify, step  # noqa: F401
+from . import quant, gemm, lmhead, verify, step, ngram  # noqa: F401
