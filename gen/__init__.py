@@ -334,3 +334,69 @@ def chain_plan(cfg: Config) -> list:
     if cfg.layers:
         return [(l.k_in, l.n_out, chain_alpha(l.k_in)) for l in chain_linears(cfg.layers)]
     return [(k, n, 1.0) for (k, n) in cfg.single]
+
+
+# ---------------------------------------------------------------- drafting inputs
+# Token histories for the prompt-lookup drafter ("Efficient LLM Challenge
+# Results", section 3: the n-gram drafter copies spans from the prompt; the
+# latency buckets of section 4 are 64, 2,048 and 8,192 prompt tokens).  A
+# history alternates fresh tokens with copies of earlier spans, so that
+# earlier occurrences of its suffixes exist, as in repetitive prompts.
+def token_history(rng, length: int, vocab: int, p_copy: float = 0.5,
+                  span_mean: float = 12.0) -> np.ndarray:
+    """int32 [length]: segments of fresh uniform tokens or copies of an earlier span."""
+    h = np.empty(length, dtype=np.int64)
+    i = 0
+    while i < length:
+        seg = max(1, int(rng.geometric(1.0 / span_mean)))
+        seg = min(seg, length - i)
+        if i > 0 and rng.random() < p_copy:
+            start = int(rng.integers(0, i))
+            for j in range(seg):                   # may overlap what it writes: a repeat
+                h[i + j] = h[start + j]
+        else:
+            h[i:i + seg] = rng.integers(0, vocab, seg)
+        i += seg
+    return h.astype(np.int32)
+
+
+def token_histories(rng, lengths, capacity: int, vocab: int, **kw) -> np.ndarray:
+    """int32 [B, capacity]: row b holds a history of lengths[b] tokens, then -1."""
+    out = np.full((len(lengths), capacity), -1, dtype=np.int32)
+    for b, n in enumerate(lengths):
+        out[b, :n] = token_history(rng, int(n), vocab, **kw)
+    return out
+
+
+def synthetic_target_next(history, vocab: int) -> int:
+    """A deterministic stand-in for the target model's greedy next token (no model
+    is available): mostly continues the most recent earlier occurrence of the last
+    two tokens, otherwise a token fixed by a hash of the last three.  Only an input
+    source for closing a draft -> verify -> append loop in tests."""
+    h = [int(t) for t in history]
+    n = len(h)
+    mix = 0x9E3779B1
+    for t in h[-3:]:
+        mix = ((mix ^ (t & 0xFFFFFFFF)) * 0x85EBCA6B) & 0xFFFFFFFF
+    if n >= 3 and (mix >> 7) % 4 != 0:
+        a, b = h[-2], h[-1]
+        for e in range(n - 2, 0, -1):
+            if h[e - 1] == a and h[e] == b:
+                return h[e + 1]
+    return (mix >> 3) % vocab
+
+
+def synthetic_target_ids(history, drafts, vocab: int) -> np.ndarray:
+    """int32 [K+1]: the stand-in target's token after the history and drafts 0..j-1,
+    for j = 0..K (a -1 draft ends the usable prefix; later rows repeat its row)."""
+    h = [int(t) for t in history]
+    out = []
+    for j in range(len(drafts) + 1):
+        out.append(synthetic_target_next(h, vocab))
+        if j < len(drafts):
+            d = int(drafts[j])
+            if d < 0:
+                out += [out[-1]] * (len(drafts) - j)
+                break
+            h.append(d)
+    return np.asarray(out, dtype=np.int32)

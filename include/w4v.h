@@ -222,6 +222,38 @@ typedef struct {
   float alpha;
 } w4v_chain_linear;
 
+/* ------------------------------------------------------------------------
+ * Prompt-lookup (n-gram) drafting (section 3, Table 3 and the paragraph on
+ * n-gram drafting: no auxiliary model, copies spans from the prompt, K fixed
+ * per deployment -- 23 for the team that used it), the step before the
+ * verify, and appending the verify's accepted tokens, the step after it.
+ *
+ * ngram_draft: for each sequence b with history h[0..L) (L = lengths[b]),
+ * for n from n_max down to n_min, the most recent earlier occurrence of the
+ * last n tokens that ends at position e <= L-2; the longest n that has one
+ * wins.  drafts[b][j] = h[e+1+j] for e+1+j < L, else -1 (constant K, the -1
+ * padding of section 3); all -1 when nothing matches.
+ *
+ * history    int32 [B x ld] (row b holds sequence b's tokens), 4-byte aligned.
+ * lengths    int32 [B]: tokens of each history (clamped to [0, ld]).
+ * n_max, n_min  1 <= n_min <= n_max <= 64.
+ * K          >= 1 drafts per sequence.
+ * drafts     int32 [B x K] out, 4-byte aligned; must not overlap history.
+ * B          >= 0 (0: nothing to do).
+ *
+ * append_accepted: history[b][L .. L+a_b] = out_tokens[b][0 .. a_b] with
+ * a_b = accepted_len[b] (clamped to [0, K]), cut at the row capacity ld;
+ * lengths[b] grows by the tokens written.  out_tokens int32 [B x (K+1)] and
+ * accepted_len int32 [B] as written by greedy_verify; K >= 0.
+ *
+ * Both are stream-ordered; argument errors return before any launch.
+ * ---------------------------------------------------------------------- */
+int ngram_draft(const int32_t* history, int64_t ld, const int32_t* lengths, int B, int n_max,
+                int n_min, int K, int32_t* drafts, void* stream);
+
+int append_accepted(int32_t* history, int64_t ld, int32_t* lengths, int B, int K,
+                    const int32_t* out_tokens, const int32_t* accepted_len, void* stream);
+
 size_t w4a16_chain_workspace_size(const w4v_chain_linear* linears, int n_linears, int M);
 
 int w4a16_chain_prepare(const w4v_chain_linear* linears, int n_linears, int M,

@@ -165,3 +165,43 @@ def test_binding_refuses_missing_library(tmp_path):
             mod.load(str(tmp_path / "missing.so"))
     finally:
         mod._lib = saved
+
+
+NGRAM_BASE = dict(h=A, ld=64, lens=A + 0x100000, B=4, n_max=4, n_min=1, K=23, d=A + 0x200000)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=0, h=None, lens=None, d=None), OK),     # nothing to do
+    (dict(B=-1), INVALID),
+    (dict(ld=0), INVALID),
+    (dict(K=0), INVALID),
+    (dict(n_min=0), INVALID),
+    (dict(n_min=3, n_max=2), INVALID),
+    (dict(n_max=65), UNSUPPORTED),
+    (dict(h=None), INVALID),
+    (dict(lens=None), INVALID),
+    (dict(d=None), INVALID),
+    (dict(h=A + 2), ALIGN),
+    (dict(d=A + 64), INVALID),                      # drafts overlap the histories
+])
+def test_ngram_draft_validation(lib, kw, status):
+    a = dict(NGRAM_BASE, **kw)
+    st = lib.ngram_draft(a["h"], a["ld"], a["lens"], a["B"], a["n_max"], a["n_min"], a["K"],
+                         a["d"], None)
+    assert st == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=0, h=None), OK),
+    (dict(B=-1), INVALID),
+    (dict(ld=0), INVALID),
+    (dict(K=-1), INVALID),
+    (dict(out=None), INVALID),
+    (dict(acc=None), INVALID),
+    (dict(out=A + 0x300002), ALIGN),
+])
+def test_append_accepted_validation(lib, kw, status):
+    a = dict(h=A, ld=64, lens=A + 0x100000, B=4, K=15, out=A + 0x300000, acc=A + 0x400000)
+    a.update(kw)
+    st = lib.append_accepted(a["h"], a["ld"], a["lens"], a["B"], a["K"], a["out"], a["acc"], None)
+    assert st == status

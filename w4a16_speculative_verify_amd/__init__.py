@@ -44,6 +44,8 @@ SIGNATURES = {
     "w8a16_lmhead_argmax": (_int, [_vp, _i64, _vp, _vp, _vp, _vp, _int, _int, _int, _vp, _sz,
                                    _vp]),
     "greedy_verify": (_int, [_vp, _vp, _int, _int, _int, _vp, _vp, _vp]),
+    "ngram_draft": (_int, [_vp, _i64, _vp, _int, _int, _int, _int, _vp, _vp]),
+    "append_accepted": (_int, [_vp, _i64, _vp, _int, _int, _vp, _vp, _vp]),
     "w8a16_lmhead_argmax_verify": (_int, [_vp, _i64, _vp, _vp, _vp, _vp, _int, _int, _vp, _int,
                                           _int, _vp, _vp, _vp, _sz, _vp]),
 }
@@ -306,3 +308,42 @@ class Chain:
         """The kernel's error word (synchronises): 0 ok, 1 wait timed out, 2 not prepared."""
         w = self.workspace[CHAIN_ERROR_OFFSET:CHAIN_ERROR_OFFSET + 4]
         return int(w.cpu().view(__import__("torch").int32).item())
+
+
+# ------------------------------------------------------------------- drafting
+def ngram_draft(history, lengths, n_max: int, n_min: int, k: int, drafts=None, stream=None):
+    """Prompt-lookup drafts int32 [B, k] (-1 padded) for histories int32 [B, ld] with
+    lengths int32 [B]."""
+    torch = _require(history, __import__("torch").int32, "history")
+    _require(lengths, torch.int32, "lengths")
+    b = history.shape[0]
+    if lengths.shape[0] != b:
+        raise ValueError("lengths must have one entry per history row")
+    if drafts is None:
+        drafts = torch.empty((b, k), dtype=torch.int32, device=history.device)
+    _require(drafts, torch.int32, "drafts")
+    if b > 0 and (drafts.shape[0] != b or drafts.shape[1] != k or drafts.stride(0) != k):
+        raise ValueError("drafts must be a contiguous int32 [B, k] tensor")
+    st = load().ngram_draft(_ptr(history), history.stride(0) if b > 0 else max(1, history.shape[1]),
+                            _ptr(lengths), b, n_max, n_min, k, _ptr(drafts), _stream(stream))
+    _check(st, "ngram_draft")
+    return drafts
+
+
+def append_accepted(history, lengths, out_tokens, accepted_len, stream=None):
+    """Append out_tokens[b][0 .. accepted_len[b]] to history row b (in place, up to the row's
+    capacity history.shape[1]); lengths grows in place."""
+    torch = _require(history, __import__("torch").int32, "history")
+    _require(lengths, torch.int32, "lengths")
+    _require(out_tokens, torch.int32, "out_tokens")
+    _require(accepted_len, torch.int32, "accepted_len")
+    b = history.shape[0]
+    if b > 0 and history.stride(0) != history.shape[1]:
+        raise ValueError("history rows must be contiguous: the row capacity is its width")
+    k = out_tokens.shape[1] - 1
+    if b > 0 and (out_tokens.shape[0] != b or out_tokens.stride(0) != k + 1):
+        raise ValueError("out_tokens must be a contiguous int32 [B, K+1] tensor")
+    st = load().append_accepted(_ptr(history), history.shape[1], _ptr(lengths), b, k,
+                                _ptr(out_tokens), _ptr(accepted_len), _stream(stream))
+    _check(st, "append_accepted")
+    return history, lengths

@@ -351,6 +351,34 @@ int w8a16_lmhead_argmax_verify(const void* h, int64_t ldh, const int8_t* w, cons
                     accepted_len, out_tokens, workspace, workspace_bytes, stream);
 }
 
+int ngram_draft(const int32_t* history, int64_t ld, const int32_t* lengths, int B, int n_max,
+                int n_min, int K, int32_t* drafts, void* stream) {
+  if (B < 0 || ld < 1 || K < 1 || n_min < 1 || n_max < n_min) return W4V_ERR_INVALID_ARG;
+  if (n_max > w4v::kNgramMaxN || ld >= (1ll << 31)) return W4V_ERR_UNSUPPORTED;
+  if (B == 0) return W4V_OK;
+  if (!history || !lengths || !drafts) return W4V_ERR_INVALID_ARG;
+  if (!aligned(history, 4) || !aligned(lengths, 4) || !aligned(drafts, 4)) return W4V_ERR_ALIGNMENT;
+  if (ranges_overlap(history, (size_t)B * ld * 4, drafts, (size_t)B * K * 4))
+    return W4V_ERR_INVALID_ARG;
+  hipError_t e = w4v::launch_ngram_draft(history, ld, lengths, B, n_max, n_min, K, drafts,
+                                         static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? W4V_OK : W4V_ERR_HIP;
+}
+
+int append_accepted(int32_t* history, int64_t ld, int32_t* lengths, int B, int K,
+                    const int32_t* out_tokens, const int32_t* accepted_len, void* stream) {
+  if (B < 0 || ld < 1 || K < 0) return W4V_ERR_INVALID_ARG;
+  if (ld >= (1ll << 31)) return W4V_ERR_UNSUPPORTED;
+  if (B == 0) return W4V_OK;
+  if (!history || !lengths || !out_tokens || !accepted_len) return W4V_ERR_INVALID_ARG;
+  if (!aligned(history, 4) || !aligned(lengths, 4) || !aligned(out_tokens, 4) ||
+      !aligned(accepted_len, 4))
+    return W4V_ERR_ALIGNMENT;
+  hipError_t e = w4v::launch_append_accepted(history, ld, lengths, B, K, out_tokens, accepted_len,
+                                             static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? W4V_OK : W4V_ERR_HIP;
+}
+
 size_t w4a16_chain_workspace_size(const w4v_chain_linear* linears, int n_linears, int M) {
   w4v::ChainLayout lay{};
   if (chain_layout(linears, n_linears, M, chain_blocks(), &lay) != W4V_OK) return 0;

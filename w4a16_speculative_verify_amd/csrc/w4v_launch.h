@@ -151,6 +151,14 @@ hipError_t launch_w4a16_chain(ChainHeader* hdr, const _Float16* x, int64_t ldx, 
                               int64_t ldy, int M, int K0, int N_last, int blocks,
                               hipStream_t stream);
 
+// ---------------------------------------------------------------- drafting
+constexpr int kNgramMaxN = 64;
+hipError_t launch_ngram_draft(const int32_t* history, int64_t ld, const int32_t* lengths, int B,
+                              int n_max, int n_min, int K, int32_t* drafts, hipStream_t stream);
+hipError_t launch_append_accepted(int32_t* history, int64_t ld, int32_t* lengths, int B, int K,
+                                  const int32_t* out_tokens, const int32_t* accepted_len,
+                                  hipStream_t stream);
+
 // ---------------------------------------------------------------- verify
 hipError_t launch_greedy_verify(const int32_t* target_ids, const int32_t* draft_ids, int B, int K,
                                 int V, int32_t* accepted_len, int32_t* out_tokens,
