@@ -15,7 +15,10 @@ measured step time); verified tokens/s and the linears' own GB/s ride along.
 ``roofline`` covers the dominant kernel (the W4A16 linear): its algorithmic
 bytes per launch over its average launch duration, timed with HIP events
 on the stream it runs on.  ``cpu_baseline`` times the numpy oracle on a
-bounded sample of the same workload on the host cores.
+bounded sample of the same workload on the host cores.  ``prefill`` (the
+M = 2048 / 8192 linears) and ``drafter`` (prompt-lookup drafting over
+8192-token histories, the step before the verify) are timed after the step,
+outside its timed region.
 """
 from __future__ import annotations
 
@@ -66,7 +69,28 @@ def cpu_baseline(wl, plan, drafts, min_seconds: float = 10.0):
             "seconds": round(dt, 2), "ms_per_step": round(1e3 * dt / steps, 1),
             "sample": f"{steps} whole verify steps of the same workload (36 layers x 4 linears "
                       f"at M=16, lm_head 2560->151936, greedy verify) through the numpy fp64 "
-                      f"oracle, {dt:.1f} s on {cores} threads"}
+                      f"oracle, {dt:.1f} s on {cores} threads",
+            "drafter": drafter_cpu()}
+
+
+def drafter_cpu():
+    """The oracle's prompt-lookup drafting on the drafter leg's B = 8 histories
+    (8192 tokens, K = 23, n 4..1), one thread: microseconds per batch."""
+    import numpy as np
+
+    import gen
+    from oracle import ngram
+
+    hist = gen.token_histories(np.random.default_rng(1008), [8192] * 8, 8192 + 64, 151936)
+    rows = [list(r[:8192]) for r in hist]
+    reps = 0
+    t0 = time.perf_counter()
+    while reps < 3 or time.perf_counter() - t0 < 1.0:
+        ngram.prompt_lookup_batch(rows, 4, 1, 23)
+        reps += 1
+    us = (time.perf_counter() - t0) / reps * 1e6
+    return {"b8_us": round(us, 1), "cores": 1,
+            "sample": f"{reps} calls on 8 histories of 8192 tokens (plain-Python oracle)"}
 
 
 def counter_traffic():
@@ -122,6 +146,47 @@ def prefill(dev, reps: int = 10):
     return out
 
 
+def drafter(dev, reps: int = 200):
+    """Prompt-lookup drafting ahead of the verify (not part of the timed step):
+    ngram_draft over B synthetic histories of 8192 tokens (half copied spans),
+    K = 23 drafts, n from 4 down to 1.  Reports the average of ``reps``
+    back-to-back calls replayed from a HIP graph and the algorithmic bytes (each
+    history read once, the drafts written) over that time."""
+    import numpy as np
+    import torch
+
+    import gen
+    import w4a16_speculative_verify_amd as w4v
+
+    length, k, n_max, n_min = 8192, 23, 4, 1
+    out = {"history_tokens": length, "k": k, "n_max": n_max, "n_min": n_min}
+    for b in (1, 8, 64):
+        rng = np.random.default_rng(1000 + b)
+        hist = torch.from_numpy(gen.token_histories(rng, [length] * b, length + 64, 151936)).to(dev)
+        lens = torch.full((b,), length, dtype=torch.int32, device=dev)
+        drafts = torch.empty((b, k), dtype=torch.int32, device=dev)
+        w4v.ngram_draft(hist, lens, n_max, n_min, k, drafts=drafts)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()                # replayed: the host call rate is not timed
+        with torch.cuda.graph(g):
+            for _ in range(reps):
+                w4v.ngram_draft(hist, lens, n_max, n_min, k, drafts=drafts)
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / reps
+        del g
+        nbytes = b * (length * 4 + 4 + k * 4)
+        out[f"b{b}"] = {"us": round(us, 2), "bytes": nbytes,
+                        "gbs": round(nbytes / (us * 1e-6) / 1e9, 1)}
+        del hist, lens, drafts
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -132,6 +197,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true",
                     help="skip the prefill-shaped (M = 2048 / 8192) GEMM timing")
+    ap.add_argument("--no-drafter", action="store_true",
+                    help="skip the prompt-lookup drafter timing")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="one device-to-device copy of this many MiB before timing (counter calibration)")
@@ -259,6 +326,11 @@ def main():
         del g_step, g_lin
         pre = prefill(dev)
 
+    draft = None
+    if not args.no_drafter:
+        print("[bench] timing the prompt-lookup drafter", file=sys.stderr, flush=True)
+        draft = drafter(dev)
+
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
@@ -298,6 +370,7 @@ def main():
                      "avg_launch_us": round(act_launch_us, 3)},
         "cpu_baseline": cpu,
         "prefill": pre,
+        "drafter": draft,
     }
     print(json.dumps(out), flush=True)
 

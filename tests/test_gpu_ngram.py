@@ -49,6 +49,42 @@ def test_long_bucket_histories(lib):
     assert np.array_equal(got, ref)
 
 
+@pytest.mark.parametrize("n_max,n_plant", [(4, 4), (4, 3), (64, 64), (64, 40)])
+def test_multi_tile_histories(lib, n_max, n_plant):
+    """Histories of 20,000+ tokens (the kernel stages 8,192 candidates at a time, newest
+    first, with 64 tokens of look-back): the only long occurrence of the suffix is planted
+    at the edges of the older tiles, where its earlier tokens sit in the look-back region,
+    while a shorter occurrence sits in the newest tile."""
+    rng = np.random.default_rng(20000 + n_max + n_plant)
+    L = 20000
+    ends = [L - 2 - 8192, L - 2 - 8191, L - 2 - 16383, L - 2 - 16384, L - 2 - 8192 - 60, n_plant - 1]
+    cap = L + 37
+    hist = rng.integers(0, 151936, (len(ends), cap)).astype(np.int32)
+    for b, e in enumerate(ends):
+        suffix = hist[b, L - n_plant:L].copy()
+        hist[b, e - n_plant + 1:e + 1] = suffix
+        # a shorter occurrence in the newest tile, which must lose to the planted one
+        hist[b, L - 300 - 1:L - 300 + 1] = suffix[-2:]
+    lengths = [L] * len(ends)
+    got = gpu_draft(lib, hist, lengths, n_max, 1, 23)
+    ref = oracle_draft(hist, lengths, n_max, 1, 23)
+    assert np.array_equal(got, ref)
+    for b, e in enumerate(ends):           # the planted occurrence is the one that wins
+        assert ngram.prompt_lookup(list(hist[b, :L]), n_max, 1, 23)[1:] == (n_plant, e)
+        assert got[b].tolist() == hist[b, e + 1:e + 24].tolist()
+
+
+def test_long_history_many_tiles(lib):
+    """Copy-heavy histories of up to 40,000 tokens over a small vocabulary, against the oracle."""
+    rng = np.random.default_rng(40000)
+    lengths = [40000, 33000, 16385, 8193, 24577]
+    hist = gen.token_histories(rng, lengths, 40000, 3000)
+    for n_max, n_min in [(4, 1), (12, 3), (64, 8)]:
+        got = gpu_draft(lib, hist, lengths, n_max, n_min, 23)
+        ref = oracle_draft(hist, lengths, n_max, n_min, 23)
+        assert np.array_equal(got, ref), (n_max, n_min)
+
+
 def test_golden_cases_on_gpu(lib):
     import json
     import os
