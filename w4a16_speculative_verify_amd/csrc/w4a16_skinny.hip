@@ -27,6 +27,8 @@
 // fixed order through LDS; with split-K > 1 the blocks of a tile publish fp32
 // partials and the last block to arrive adds them in split order, so the
 // output does not depend on arrival order.
+#include <type_traits>
+
 #include "w4v_device.h"
 #include "w4v_launch.h"
 
@@ -90,7 +92,9 @@ __device__ __forceinline__ void store_row4(_Float16* dst, float a0, float a1, fl
   *reinterpret_cast<u32x2*>(dst) = v;
 }
 
-template <int MT, int WT, int WK, int D>
+// SB: split-K partials the last block of a tile loads per batch (one round
+// trip to memory per batch; loads past the last split are masked off)
+template <int MT, int WT, int WK, int D, int SB>
 __global__ __launch_bounds__(64 * WT * WK) void w4a16_skinny_kernel(GemmArgs a, int splits,
                                                                     unsigned* tickets,
                                                                     float* partials) {
@@ -165,64 +169,73 @@ __global__ __launch_bounds__(64 * WT * WK) void w4a16_skinny_kernel(GemmArgs a, 
     __builtin_amdgcn_sched_barrier(0);
   }
 
-  // Steps are padded to a multiple of D so that the loop body has no branch
-  // around loads or barriers (a padding step loads nothing and computes
-  // nothing); a branch there would make the compiler drain the loads at
-  // every iteration.
-  const int nsteps = (nmax + D - 1) / D * D;
-  for (int j0 = 0; j0 < nsteps; j0 += D) {
+  // One step per group: ring slot i (a compile-time index) is computed and
+  // then refilled D groups ahead.  The loop body runs whole rounds of D
+  // steps with no branch around loads or barriers (a branch there would make
+  // the compiler drain the loads at every iteration); the last nmax % D steps
+  // follow the loop, where draining costs nothing.  Steps past a wave's own
+  // groups (k-slices of unequal length) load nothing and compute nothing but
+  // still take the block barrier.
+  auto step = [&](auto slot, const int j) __attribute__((always_inline)) {
+    constexpr int i = decltype(slot)::value;
+    // share the group's activations: this wave's chunks, reordered to the
+    // k order of the dequantised nibbles, into the LDS tile
+    uint32_t* xt = xtile(j & 1, wk);
 #pragma unroll
-    for (int i = 0; i < D; ++i) {
-      const int j = j0 + i;
-      // share the group's activations: this wave's chunks, reordered to the
-      // k order of the dequantised nibbles, into the LDS tile
-      uint32_t* xt = xtile(j & 1, wk);
+    for (int q = 0; q < Frag<MT, WT>::kXLoads; ++q)
+      *reinterpret_cast<f16x8*>(xt + xrow_of(q * WT + wt, lane) * kXRowWords + chunk * 4) =
+          permute_for_int4(f[i].x[q]);
+    lds_barrier();
+    if (j < n) {                                  // wave-uniform
+      ZeroPair zz[4];
 #pragma unroll
-      for (int q = 0; q < Frag<MT, WT>::kXLoads; ++q)
-        *reinterpret_cast<f16x8*>(xt + xrow_of(q * WT + wt, lane) * kXRowWords + chunk * 4) =
-            permute_for_int4(f[i].x[q]);
-      lds_barrier();
-      if (j < n) {                                  // wave-uniform
-        ZeroPair zz[4];
+      for (int c = 0; c < 4; ++c) zz[c] = zero_pair((f[i].zw >> (zshift + 4 * c)) & 0xFu);
+      f32x4 tmp[MT][4];
 #pragma unroll
-        for (int c = 0; c < 4; ++c) zz[c] = zero_pair((f[i].zw >> (zshift + 4 * c)) & 0xFu);
-        f32x4 tmp[MT][4];
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) tmp[mt][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int it = 0; it < 4; ++it) {
+        // A layout: row l % 16, k = 32 it + 8 (l / 16) .. + 7
+        f16x8 av[MT];
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
+          av[mt] = *reinterpret_cast<const f16x8*>(xt + (mt * 16 + chunk) * kXRowWords +
+                                                   (it * 4 + kb) * 4);
 #pragma unroll
-          for (int c = 0; c < 4; ++c) tmp[mt][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int c = 0; c < 4; ++c) {
+          const f16x8 b = dequant_int4_word(f[i].w[it][c], zz[c], magic);
 #pragma unroll
-        for (int it = 0; it < 4; ++it) {
-          // A layout: row l % 16, k = 32 it + 8 (l / 16) .. + 7
-          f16x8 av[MT];
-#pragma unroll
-          for (int mt = 0; mt < MT; ++mt)
-            av[mt] = *reinterpret_cast<const f16x8*>(xt + (mt * 16 + chunk) * kXRowWords +
-                                                     (it * 4 + kb) * 4);
-#pragma unroll
-          for (int c = 0; c < 4; ++c) {
-            const f16x8 b = dequant_int4_word(f[i].w[it][c], zz[c], magic);
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt) tmp[mt][c] = mfma16x16x32(av[mt], b, tmp[mt][c]);
-          }
+          for (int mt = 0; mt < MT; ++mt) tmp[mt][c] = mfma16x16x32(av[mt], b, tmp[mt][c]);
         }
-        // copy the vector elements to scalars before the bit casts: a bit
-        // cast of an ext-vector element expression reads element 0 with
-        // this compiler
-        const uint32_t s_lo = f[i].s.x, s_hi = f[i].s.y;
-        const f16x2 s01 = __builtin_bit_cast(f16x2, s_lo);
-        const f16x2 s23 = __builtin_bit_cast(f16x2, s_hi);
-        const float sc[4] = {(float)s01.x, (float)s01.y, (float)s23.x, (float)s23.y};
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-          for (int c = 0; c < 4; ++c)
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-              acc[mt][c][r] = __builtin_fmaf(sc[c], tmp[mt][c][r], acc[mt][c][r]);
       }
-      load_group<MT, WT>(f[i], rs, o, group_of(j + D), j + D < n);
+      // copy the vector elements to scalars before the bit casts: a bit
+      // cast of an ext-vector element expression reads element 0 with
+      // this compiler
+      const uint32_t s_lo = f[i].s.x, s_hi = f[i].s.y;
+      const f16x2 s01 = __builtin_bit_cast(f16x2, s_lo);
+      const f16x2 s23 = __builtin_bit_cast(f16x2, s_hi);
+      const float sc[4] = {(float)s01.x, (float)s01.y, (float)s23.x, (float)s23.y};
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            acc[mt][c][r] = __builtin_fmaf(sc[c], tmp[mt][c][r], acc[mt][c][r]);
     }
+    load_group<MT, WT>(f[i], rs, o, group_of(j + D), j + D < n);
+  };
+  int j0 = 0;
+  for (; j0 + D <= nmax; j0 += D) {
+    step(std::integral_constant<int, 0>{}, j0);
+    step(std::integral_constant<int, 1>{}, j0 + 1);
+    if constexpr (D > 2) step(std::integral_constant<int, 2>{}, j0 + 2);
+  }
+  if (j0 < nmax) step(std::integral_constant<int, 0>{}, j0);                 // block-uniform
+  if constexpr (D > 2) {
+    if (j0 + 1 < nmax) step(std::integral_constant<int, 1>{}, j0 + 1);
   }
 
   // ---- add the k-slices of each tile in fixed order through LDS
@@ -315,17 +328,17 @@ __global__ __launch_bounds__(64 * WT * WK) void w4a16_skinny_kernel(GemmArgs a, 
     if (mr < 0) continue;
     const int m = row_of(mr);
     const int mloc = m - mbase;
-    // partials in split order, eight loads in flight at a time
+    // partials in split order, SB loads in flight per batch
     f32x4 sum = {0.f, 0.f, 0.f, 0.f};
-    for (int sp0 = 0; sp0 < splits; sp0 += 8) {
-      u32x4 v[8];
+    for (int sp0 = 0; sp0 < splits; sp0 += SB) {
+      u32x4 v[SB];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int sp = sp0 + u < splits ? sp0 + u : splits - 1;
-        v[u] = ld_agent_x4(pr, (uint32_t)((((size_t)sp * rows_blk + mloc) * ncols + pcol) * 4));
-      }
+      for (int u = 0; u < SB; ++u)
+        v[u] = ld_agent_x4(pr, sp0 + u < splits
+                                   ? (uint32_t)((((size_t)(sp0 + u) * rows_blk + mloc) * ncols + pcol) * 4)
+                                   : kNoLoad);
 #pragma unroll
-      for (int u = 0; u < 8; ++u)
+      for (int u = 0; u < SB; ++u)
         if (sp0 + u < splits) sum += __builtin_bit_cast(f32x4, v[u]);
     }
     if (colok && m < a.M)
@@ -334,18 +347,19 @@ __global__ __launch_bounds__(64 * WT * WK) void w4a16_skinny_kernel(GemmArgs a, 
   }
 }
 
-template <int MT, int WT, int WK, int D>
+template <int MT, int WT, int WK, int D, int SB>
 void launch_t(const GemmArgs& a, const GemmPlan& p, unsigned* tickets, float* partials,
               hipStream_t stream) {
-  hipLaunchKernelGGL((w4a16_skinny_kernel<MT, WT, WK, D>), dim3(p.col_blocks, p.splits, p.mblocks),
+  hipLaunchKernelGGL((w4a16_skinny_kernel<MT, WT, WK, D, SB>), dim3(p.col_blocks, p.splits, p.mblocks),
                      dim3(64 * WT * WK), 0, stream, a, p.splits, tickets, partials);
 }
 
 template <int MT, int WT, int WK>
 void launch_wk(const GemmArgs& a, const GemmPlan& p, unsigned* tickets, float* partials,
                hipStream_t stream) {
-  if (p.depth <= 2) launch_t<MT, WT, WK, 2>(a, p, tickets, partials, stream);
-  else launch_t<MT, WT, WK, 3>(a, p, tickets, partials, stream);
+  // three groups in flight per wave; one batch of partial loads up to 8 splits
+  if (p.splits <= 8) launch_t<MT, WT, WK, 3, 8>(a, p, tickets, partials, stream);
+  else launch_t<MT, WT, WK, 3, 16>(a, p, tickets, partials, stream);
 }
 
 template <int MT>

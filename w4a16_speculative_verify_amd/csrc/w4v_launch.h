@@ -45,7 +45,7 @@ struct GemmPlan {
   int wk;            // k-slices per block (wt * wk = 4 or 8 waves)
   int col_blocks;    // ceil(tiles / wt)
   int splits;        // split-K factor across blocks (1 = none)
-  int depth;         // groups in flight per wave (2 or 3)
+  int depth;         // groups in flight per wave (3)
   size_t ticket_bytes;
   size_t partial_bytes;
   size_t workspace_bytes() const { return ticket_bytes + partial_bytes; }
