@@ -16,9 +16,10 @@ measured step time); verified tokens/s and the linears' own GB/s ride along.
 bytes per launch over its average launch duration, timed with HIP events
 on the stream it runs on.  ``cpu_baseline`` times the numpy oracle on a
 bounded sample of the same workload on the host cores.  ``prefill`` (the
-M = 2048 / 8192 linears) and ``drafter`` (prompt-lookup drafting over
-8192-token histories, the step before the verify) are timed after the step,
-outside its timed region.
+M = 2048 / 8192 linears), ``drafter`` (prompt-lookup drafting over
+8192-token histories, the step before the verify) and ``drafter_int4_step``
+(a 4-bit drafter's 21 linears at M = 16) are timed after the step, outside
+its timed region.
 """
 from __future__ import annotations
 
@@ -146,6 +147,44 @@ def prefill(dev, reps: int = 10):
     return out
 
 
+def drafter_gemm(dev, reps: int = 20):
+    """The 4-bit drafter's step through the same W4A16 linear: the 12800 -> 2560
+    fusion of five tapped hidden states, then five layers of the target's four
+    linears, at M = 16 (279.2 MB of weights, scales and zeros), replayed from a
+    HIP graph; average of ``reps`` replays."""
+    import torch
+
+    import gen
+    from w4a16_speculative_verify_amd.step import DeviceLinear, VerifyStep
+
+    wl = gen.make_drafter_workload()
+    up = lambda a: torch.from_numpy(a).to(dev)
+    plan = gen.drafter_plan()
+    lins = [DeviceLinear(up(l.qweight), up(l.scales), up(l.qzeros), k, n, a)
+            for l, (k, n, a) in zip(wl.linears, plan)]
+    step = VerifyStep(lins, None, None, 16, 1, 15, device=dev)
+    x = up(wl.x)
+    step.linears_only(x)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step.linears_only(x)
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / reps
+    nbytes = sum(linear_bytes(16, k, n) for k, n, _ in plan)
+    gbs = nbytes / (us * 1e-6) / 1e9
+    del g, step, lins
+    return {"linears": len(plan), "m": 16, "us_per_step": round(us, 2), "bytes": nbytes,
+            "gbs": round(gbs, 1), "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2)}
+
+
 def drafter(dev, reps: int = 200):
     """Prompt-lookup drafting ahead of the verify (not part of the timed step):
     ngram_draft over B synthetic histories of 8192 tokens (half copied spans),
@@ -198,7 +237,7 @@ def main():
     ap.add_argument("--no-prefill", action="store_true",
                     help="skip the prefill-shaped (M = 2048 / 8192) GEMM timing")
     ap.add_argument("--no-drafter", action="store_true",
-                    help="skip the prompt-lookup drafter timing")
+                    help="skip the drafter timings (prompt lookup, 4-bit drafter step)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="one device-to-device copy of this many MiB before timing (counter calibration)")
@@ -326,6 +365,11 @@ def main():
         del g_step, g_lin
         pre = prefill(dev)
 
+    dgemm = None
+    if not args.no_drafter:
+        print("[bench] timing the 4-bit drafter step", file=sys.stderr, flush=True)
+        dgemm = drafter_gemm(dev)
+
     draft = None
     if not args.no_drafter:
         print("[bench] timing the prompt-lookup drafter", file=sys.stderr, flush=True)
@@ -371,6 +415,7 @@ def main():
         "cpu_baseline": cpu,
         "prefill": pre,
         "drafter": draft,
+        "drafter_int4_step": dgemm,
     }
     print(json.dumps(out), flush=True)
 

@@ -336,6 +336,38 @@ def chain_plan(cfg: Config) -> list:
     return [(k, n, 1.0) for (k, n) in cfg.single]
 
 
+# ---------------------------------------------------------------- drafter step
+# A 4-bit drafter (W4A16 GPTQ, group size 128, 277 MB, five layers; results
+# page, section 5) makes every draft step an INT4 GEMM.  The page gives only
+# its size.  Reading: five layers with the target's four linears, preceded by
+# one linear that fuses the hidden states of five tapped target layers
+# (5 x 2560 -> 2560), run on a block of 16 rows: 279.2 MB of weights, scales
+# and zeros, within 1% of the page's figure.
+DRAFTER_TAPS = 5
+DRAFTER_LAYERS = 5
+DRAFTER_FUSE = Linear("fuse", DRAFTER_TAPS * HIDDEN, HIDDEN)
+DRAFTER_CONFIG = Config(0, "drafter_step", m=16, layers=DRAFTER_LAYERS, vocab=0,
+                        note="fusion 12800->2560 + 5 layers of the target's linears at M=16")
+
+
+def drafter_linears() -> list:
+    return [DRAFTER_FUSE] + chain_linears(DRAFTER_LAYERS)
+
+
+def drafter_plan() -> list:
+    """(k_in, n_out, alpha) of the drafter's linears in execution order."""
+    return [(l.k_in, l.n_out, chain_alpha(l.k_in)) for l in drafter_linears()]
+
+
+def make_drafter_workload(seed_offset: int = 0, m: int = 16) -> Workload:
+    """Seeded drafter linears and a fused-feature input block (fp16 [m, 12800]).
+    Seeds: SeedSequence(900 + seed_offset).spawn(2) -> [activations, weights]."""
+    r_x, r_w = streams(900 + seed_offset, 2)
+    linears = [qlinear(r_w, l.k_in, l.n_out) for l in drafter_linears()]
+    x = activations(r_x, m, DRAFTER_FUSE.k_in)
+    return Workload(DRAFTER_CONFIG, x, linears)
+
+
 # ---------------------------------------------------------------- drafting inputs
 # Token histories for the prompt-lookup drafter ("Efficient LLM Challenge
 # Results", section 3: the n-gram drafter copies spans from the prompt; the

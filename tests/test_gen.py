@@ -119,3 +119,28 @@ def test_config_shapes():
     per_layer = sum(k * n // 2 + (k // 128) * n * 2 + (k // 128) * n // 2 for k, n, _ in plan3[:4])
     assert per_layer * 36 == 1_887_621_120
     assert gen.chain_plan(gen.CONFIGS[5]) == [(2560, 19456, 1.0), (9728, 2560, 1.0)]
+
+
+def test_drafter_reading_matches_page_size():
+    """The 4-bit drafter reading (fusion of five 2560-wide taps, then five layers of the
+    target's linears) holds 279.2 MB of weights, scales and zeros: within 1% of the
+    277 MB the results page gives for team #3's W4A16 g128 drafter (section 5)."""
+    lins = gen.drafter_linears()
+    assert len(lins) == 1 + 4 * gen.DRAFTER_LAYERS
+    assert (lins[0].k_in, lins[0].n_out) == (5 * gen.HIDDEN, gen.HIDDEN)
+    total = sum(l.k_in * l.n_out // 2 + (l.k_in // 128) * l.n_out * 2
+                + (l.k_in // 128) * (l.n_out // 8) * 4 for l in lins)
+    assert total == 279_193_600
+    assert abs(total / 277e6 - 1) < 0.01
+    # each linear reads the leading columns of the previous output
+    for prev, cur in zip(lins, lins[1:]):
+        assert cur.k_in <= prev.n_out
+
+
+def test_drafter_workload_is_seeded():
+    a = gen.make_drafter_workload()
+    b = gen.make_drafter_workload()
+    assert a.x.shape == (16, 5 * gen.HIDDEN) and a.x.dtype == np.float16
+    assert a.x.tobytes() == b.x.tobytes()
+    assert all(la.qweight.tobytes() == lb.qweight.tobytes() for la, lb in zip(a.linears, b.linears))
+    assert [p[:2] for p in gen.drafter_plan()] == [(l.k_in, l.n_out) for l in gen.drafter_linears()]
