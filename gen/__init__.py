@@ -147,25 +147,26 @@ def lmhead_scales(rng, v: int) -> np.ndarray:
 
 @dataclass
 class QLinear:
-    """Packed W4A16 linear in the canonical layout."""
+    """Packed W4A16 linear in the canonical layout (g = group size)."""
     qweight: np.ndarray   # int32 [k/8, n]
-    scales: np.ndarray    # fp16 [k/128, n]
-    qzeros: np.ndarray    # int32 [k/128, n/8]
+    scales: np.ndarray    # fp16 [k/g, n]
+    qzeros: np.ndarray    # int32 [k/g, n/8]
     k: int
     n: int
+    group_size: int = GROUP
 
     @property
     def nbytes(self) -> int:
         return self.qweight.nbytes + self.scales.nbytes + self.qzeros.nbytes
 
 
-def qlinear(rng, k: int, n: int) -> QLinear:
-    g = k // GROUP
+def qlinear(rng, k: int, n: int, group_size: int = GROUP) -> QLinear:
+    g = k // group_size
     # fixed draw order: words, scales, zeros
     qw = qweight_words(rng, k, n)
     sc = group_scales(rng, g, n)
     qz = qzero_words(rng, g, n)
-    return QLinear(qw, sc, qz, k, n)
+    return QLinear(qw, sc, qz, k, n, group_size)
 
 
 # --------------------------------------------------------------------------

@@ -117,3 +117,24 @@ def test_fp16_storage_rounds_to_nearest_even():
     assert np.isinf(got[5])
     assert got[6] == 0.0
     assert got[7] == np.float16(2.0 ** -24)
+
+
+def test_brute_force_exact_rationals_group_32():
+    rng = np.random.default_rng(23)
+    m, k, n = 2, 128, 16
+    lin = gen.qlinear(rng, k, n, group_size=32)
+    assert lin.scales.shape == (4, n) and lin.qzeros.shape == (4, n // 8)
+    x = gen.activations(rng, m, k)
+    y = gemm.w4a16_gemm(x, lin.qweight, lin.scales, lin.qzeros, alpha=1.25, group_size=32)
+    words = lin.qweight.view(np.uint32)
+    zwords = lin.qzeros.view(np.uint32)
+    for mm in range(m):
+        for nn in range(n):
+            acc = Fraction(0)
+            for kk in range(k):
+                qv = (int(words[kk // 8, nn]) >> (4 * (kk % 8))) & 15
+                zv = (int(zwords[kk // 32, nn // 8]) >> (4 * (nn % 8))) & 15
+                sv = Fraction(float(lin.scales[kk // 32, nn]))
+                acc += Fraction(float(x[mm, kk])) * sv * (qv - zv)
+            exact = Fraction(1.25) * acc
+            assert abs(y[mm, nn] - float(exact)) <= 1e-12 * max(1.0, abs(float(exact)))

@@ -93,3 +93,25 @@ def test_dequantize_columns_matches_full():
     cols = np.array([0, 7, 8, 33, 63])
     assert np.array_equal(quant.dequantize_columns(lin.qweight, lin.scales, lin.qzeros, cols),
                           full[:, cols])
+
+
+def test_group_to_scale_mapping_at_boundaries_group_32():
+    # Group size 32 (results page, section 5: team #5's compressed-tensors target):
+    # row k carries the scale and zero-point of group k // 32, including k = 31, 32, 63, 64.
+    k, n = 256, 8
+    q = np.full((k, n), 9, dtype=np.int64)
+    z = np.empty((k // 32, n), dtype=np.int64)
+    s = np.empty((k // 32, n), dtype=np.float16)
+    for g in range(k // 32):
+        z[g, :] = 8 - (g % 3)                     # q - z = 1 + g % 3
+        s[g, :] = 2.0 ** -(g + 3)
+        s[g, 5] = 2.0 ** -g
+    w = quant.dequantize(gen.pack_int4_along_k(q), s, gen.pack_int4_along_n(z), group_size=32)
+    for kk in (0, 31, 32, 63, 64, 95, 96, 127, 128, 255):
+        g = kk // 32
+        assert w[kk, 5] == (1 + g % 3) * 2.0 ** -g
+        assert w[kk, 0] == (1 + g % 3) * 2.0 ** -(g + 3)
+    cols = np.array([0, 5, 7])
+    assert np.array_equal(quant.dequantize_columns(gen.pack_int4_along_k(q), s,
+                                                   gen.pack_int4_along_n(z), cols, group_size=32),
+                          w[:, cols])
