@@ -56,9 +56,11 @@ const char* w4v_status_string(int status);
 int w4v_abi_version(void);
 
 /* ------------------------------------------------------------------------
- * W4A16 linear (section 3: 4-bit weights, group size 128, 16-bit activations)
+ * W4A16 linear (section 3: 4-bit weights, group size 128, 16-bit activations;
+ * section 5: group size 32 for team #5's compressed-tensors target)
  *
- *   y[m, n] = fp16_rne( alpha * sum_k x[m, k] * s[k/128, n] * (q[k, n] - z[k/128, n]) )
+ *   y[m, n] = fp16_rne( alpha * sum_k x[m, k] * s[k/g, n] * (q[k, n] - z[k/g, n]) ),
+ *   g = group_size
  *
  * x        fp16  [M x K], row stride ldx >= K; 16-byte aligned, ldx % 8 == 0.
  * qweight  int32 [K/8 x N]: nibble j (bits 4j..4j+3) of word (i, n) is
@@ -69,14 +71,15 @@ int w4v_abi_version(void);
  * y        fp16  [M x N] out, row stride ldy >= N; 16-byte aligned, ldy % 8 == 0.
  *          y must not overlap x.
  * Sizes    M >= 0 (M == 0 or N == 0: nothing to do, W4V_OK), K > 0,
- *          N % 8 == 0, K % group_size == 0; group_size must be 128
- *          (W4V_ERR_UNSUPPORTED otherwise).  For M < 512 the packed weights
+ *          N % 8 == 0, K % group_size == 0; group_size must be 128 or 32,
+ *          and K % 128 == 0 for both (W4V_ERR_UNSUPPORTED otherwise: the
+ *          kernels step 128 k at a time).  For M < 512 the packed weights
  *          (K*N/2 bytes), the scales and the rows of x (M*ldx*2 bytes) must
  *          each stay below 2 GiB (W4V_ERR_UNSUPPORTED otherwise).
  * alpha    epilogue scale applied to the fp32 accumulator before the single
  *          round-to-nearest-even to fp16.
- * Paths    M <= 32: weights dequantised exactly in registers, group scale
- *          applied to the fp32 group sum (split-K across blocks).
+ * Paths    M <= 32: weights dequantised exactly in registers, each group's
+ *          scale applied to that group's fp32 sum (split-K across blocks).
  *          33 <= M < 512: the same arithmetic in an LDS-tiled MFMA kernel.
  *          M >= 512 (prefill shapes, bound by the matrix cores): the weights
  *          are first expanded to fp16 by this library's kernel,

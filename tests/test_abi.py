@@ -57,6 +57,9 @@ def gemm(lib, x=A, ldx=2560, qw=A, sc=A, qz=A, y=A * 64, ldy=2560, M=16, N=2560,
 @pytest.mark.parametrize("kw,status", [
     (dict(g=64), UNSUPPORTED),
     (dict(g=0), INVALID),
+    (dict(g=32, K=96, ldx=128), UNSUPPORTED),     # group size 32 needs K % 128 == 0
+    (dict(g=32, K=100, ldx=128), INVALID),        # K not a multiple of the group size
+    (dict(g=32, x=A + 2), ALIGN),                 # group size 32 reaches the pointer checks
     (dict(K=100, ldx=128), INVALID),
     (dict(K=0), INVALID),
     (dict(N=12, ldy=16), INVALID),
@@ -89,6 +92,10 @@ def test_gemm_workspace(lib):
     assert gemm(lib, K=4096, ldx=4096, ws=A * 256 + 16, wsb=need) == ALIGN
     assert w4v.gemm_workspace_size(0, 2560, 4096) == 0
     assert w4v.gemm_workspace_size(16, 2560, 4096, 64) == 0
+    # group size 32 runs the same plans
+    assert w4v.gemm_workspace_size(16, 2560, 4096, 32) == need
+    assert w4v.gemm_workspace_size(16, 2560, 96, 32) == 0
+    assert gemm(lib, K=4096, ldx=4096, g=32, ws=None, wsb=0) == WORKSPACE
     # sizes are a function of the shape alone
     assert w4v.gemm_workspace_size(16, 2560, 4096) == need
 

@@ -148,8 +148,9 @@ def w4a16_gemm(x, qweight, scales, qzeros, alpha: float = 1.0, out=None, workspa
     """y[M, N] = fp16(alpha * x[:, :K] @ dequant(qweight, scales, qzeros)).
 
     x: fp16 [M, >=K] (a column slice of a wider tensor is fine: its row stride
-    is passed as ldx); qweight: int32 [K/8, N]; scales: fp16 [K/128, N];
-    qzeros: int32 [K/128, N/8].  ``out`` may be a row-strided fp16 [M, N] view.
+    is passed as ldx); qweight: int32 [K/8, N]; scales: fp16 [K/g, N];
+    qzeros: int32 [K/g, N/8] with g = group_size (128 or 32).  ``out`` may be a
+    row-strided fp16 [M, N] view.
     """
     torch = _require(x, __import__("torch").float16, "x")
     _require(qweight, torch.int32, "qweight")
@@ -160,6 +161,10 @@ def w4a16_gemm(x, qweight, scales, qzeros, alpha: float = 1.0, out=None, workspa
     m = x.shape[0]
     if x.shape[1] < k:
         raise ValueError(f"x has {x.shape[1]} columns, the weights need {k}")
+    if group_size > 0 and k % group_size == 0 and (
+            tuple(scales.shape) != (k // group_size, n) or tuple(qzeros.shape) != (k // group_size, n // 8)):
+        raise ValueError(f"scales {tuple(scales.shape)} / qzeros {tuple(qzeros.shape)} do not fit "
+                         f"K={k}, N={n} at group size {group_size}")
     if out is None:
         out = torch.empty((m, n), dtype=torch.float16, device=x.device)
     _require(out, torch.float16, "out")

@@ -30,8 +30,9 @@ int gemm_check(const void* x, int64_t ldx, const int32_t* qweight, const void* s
                const int32_t* qzeros, const void* y, int64_t ldy, int M, int N, int K,
                int group_size) {
   if (M < 0 || N < 0 || K <= 0 || group_size <= 0) return W4V_ERR_INVALID_ARG;
-  if (group_size != w4v::kGroup) return W4V_ERR_UNSUPPORTED;
+  if (group_size != w4v::kGroup && group_size != 32) return W4V_ERR_UNSUPPORTED;
   if (K % group_size != 0 || N % 8 != 0) return W4V_ERR_INVALID_ARG;
+  if (K % w4v::kGroup != 0) return W4V_ERR_UNSUPPORTED;   // the kernels step 128 k at a time
   if (M == 0 || N == 0) return W4V_OK;
   if (!x || !qweight || !scales || !qzeros || !y) return W4V_ERR_INVALID_ARG;
   if (ldx < K || ldy < N) return W4V_ERR_INVALID_ARG;
@@ -219,7 +220,7 @@ const char* w4v_status_string(int status) {
   switch (status) {
     case W4V_OK: return "ok";
     case W4V_ERR_INVALID_ARG: return "invalid argument (null pointer, size or stride)";
-    case W4V_ERR_UNSUPPORTED: return "unsupported request (e.g. group_size other than 128)";
+    case W4V_ERR_UNSUPPORTED: return "unsupported request (e.g. group_size other than 128 or 32)";
     case W4V_ERR_ALIGNMENT: return "pointer or stride breaks the required alignment";
     case W4V_ERR_WORKSPACE: return "workspace missing or smaller than required";
     case W4V_ERR_HIP: return "HIP runtime error";
@@ -240,8 +241,8 @@ static size_t lib_workspace_bytes(int N, int K) {
 }
 
 size_t w4a16_gemm_workspace_size(int M, int N, int K, int group_size) {
-  if (M <= 0 || N <= 0 || K <= 0 || group_size != w4v::kGroup || K % group_size != 0 ||
-      N % 8 != 0)
+  if (M <= 0 || N <= 0 || K <= 0 || (group_size != w4v::kGroup && group_size != 32) ||
+      K % w4v::kGroup != 0 || N % 8 != 0)
     return 0;
   if (M >= w4v::kLibMinRows) return lib_workspace_bytes(N, K);
   if (M >= w4v::kTiledMinRows) return 0;
@@ -258,7 +259,7 @@ int w4a16_gemm(const void* x, int64_t ldx, const int32_t* qweight, const void* s
   if (tiled && (M + 127) / 128 > kMaxGridYZ) return W4V_ERR_UNSUPPORTED;
   // buffer resources take 32-bit offsets below 2 GiB
   const bool big = (size_t)K * N / 2 >= (1ull << 31) || (size_t)M * ldx * 2 >= (1ull << 31) ||
-                   (size_t)K / 128 * N * 2 >= (1ull << 31);
+                   (size_t)(K / group_size) * N * 2 >= (1ull << 31);
   if (tiled && !lib && big) return W4V_ERR_UNSUPPORTED;
   if (lib) {
     st = workspace_check(lib_workspace_bytes(N, K), workspace, workspace_bytes);
@@ -285,6 +286,7 @@ int w4a16_gemm(const void* x, int64_t ldx, const int32_t* qweight, const void* s
   a.N = N;
   a.K = K;
   a.alpha = alpha;
+  a.group_size = group_size;
   const hipStream_t s = static_cast<hipStream_t>(stream);
   if (lib) {
     // weights to fp16 (our kernel), then the plain GEMM; if the library has
@@ -292,7 +294,8 @@ int w4a16_gemm(const void* x, int64_t ldx, const int32_t* qweight, const void* s
     // anyway), the LDS-tiled kernel computes the same product
     char* base = static_cast<char*>(workspace) + lib_offset();
     _Float16* wt = reinterpret_cast<_Float16*>(base);
-    hipError_t e = w4v::launch_dequant_w4_f16t(a.qweight, a.scales, a.qzeros, K, N, wt, s);
+    hipError_t e = w4v::launch_dequant_w4_f16t(a.qweight, a.scales, a.qzeros, K, N, group_size,
+                                               wt, s);
     if (e != hipSuccess) return W4V_ERR_HIP;
     if (w4v::lib_gemm_f16_tn(a.x, ldx, wt, a.y, ldy, M, N, K, alpha,
                              base + lib_weights_bytes(N, K), w4v::kLibWorkspace, s))

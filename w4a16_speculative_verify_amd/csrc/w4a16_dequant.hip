@@ -4,14 +4,15 @@
 // matrix cores, and a plain fp16 GEMM on dequantised weights runs it at
 // about twice the rate of the fused in-register kernel (measured on MI355X).
 //
-//   wt[n, k] = fp16_rne( float(s[k/128, n]) * (q[k, n] - z[k/128, n]) )
+//   wt[n, k] = fp16_rne( float(s[k/gs, n]) * (q[k, n] - z[k/gs, n]) ),  gs = 128 or 32
 //
 // written transposed (row n holds all K values of column n), the layout in
 // which both GEMM operands are contiguous along k.  The product in fp32 is
 // exact (an 11-bit scale times a 5-bit integer), so each weight is rounded
 // once.  HBM-bound: K*N/2 + scales + zeros read, 2*K*N written.
 //
-// A block expands one 128-k group of 64 columns: its 16 x 64 packed words are
+// A block expands 128 k of 64 columns (one group, or four of 32 k: wave w's
+// four packed rows then form group 4 * step + w): its 16 x 64 packed words are
 // read row by row (each wave instruction covers 256 contiguous bytes), the
 // 64 x 128 fp16 values are transposed through LDS, and each output row's 256
 // bytes are written by 16 adjacent lanes.
@@ -27,7 +28,7 @@ constexpr int kRowHalves = kGroup + 8;      // LDS row: 128 k + 16 bytes of padd
 
 __global__ __launch_bounds__(256) void dequant_w4_f16t_kernel(
     const uint32_t* __restrict__ qweight, const _Float16* __restrict__ scales,
-    const uint32_t* __restrict__ qzeros, int K, int N, _Float16* __restrict__ wt) {
+    const uint32_t* __restrict__ qzeros, int K, int N, int q4, _Float16* __restrict__ wt) {
   __shared__ _Float16 tile[kCols * kRowHalves];
   const int t = threadIdx.x;
   const int g = blockIdx.y;
@@ -35,8 +36,9 @@ __global__ __launch_bounds__(256) void dequant_w4_f16t_kernel(
   const int nl = t & (kCols - 1), wave = t >> 6;
   const int n = n0 + nl;
   if (n < N) {
-    const float s = (float)scales[(size_t)g * N + n];
-    const int z = (int)((qzeros[(size_t)g * (N >> 3) + (n >> 3)] >> (4 * (n & 7))) & 0xFu);
+    const int qg = q4 ? 4 * g + wave : g;           // quantisation group of this wave's rows
+    const float s = (float)scales[(size_t)qg * N + n];
+    const int z = (int)((qzeros[(size_t)qg * (N >> 3) + (n >> 3)] >> (4 * (n & 7))) & 0xFu);
     uint32_t w[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) w[r] = qweight[(size_t)(g * 16 + wave * 4 + r) * N + n];
@@ -66,11 +68,11 @@ __global__ __launch_bounds__(256) void dequant_w4_f16t_kernel(
 }  // namespace
 
 hipError_t launch_dequant_w4_f16t(const uint32_t* qweight, const _Float16* scales,
-                                  const uint32_t* qzeros, int K, int N, _Float16* wt,
-                                  hipStream_t stream) {
+                                  const uint32_t* qzeros, int K, int N, int group_size,
+                                  _Float16* wt, hipStream_t stream) {
   const dim3 grid((N + kCols - 1) / kCols, K / kGroup);
   hipLaunchKernelGGL(dequant_w4_f16t_kernel, grid, dim3(256), 0, stream, qweight,
-                     scales, qzeros, K, N, wt);
+                     scales, qzeros, K, N, group_size == 32 ? 1 : 0, wt);
   return hipGetLastError();
 }
 

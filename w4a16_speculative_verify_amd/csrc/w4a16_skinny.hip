@@ -46,13 +46,15 @@ struct Resources {
 // bytes so that 8 lanes reading one 16-byte column hit distinct banks
 constexpr int kXRowWords = (kGroup * 2 + 16) / 4;
 
-template <int MT, int WT>
+// One 128-k step holds Q quantisation groups (Q = 1: group size 128; Q = 4:
+// group size 32, one per 32-k MFMA slab).
+template <int MT, int WT, int Q>
 struct Frag {
-  static constexpr int kXLoads = 4 * MT / WT;   // activation loads of this wave per group
+  static constexpr int kXLoads = 4 * MT / WT;   // activation loads of this wave per step
   u32x4 w[4];            // 4 quads of packed rows, 4 columns each
-  uint32_t zw;           // zero-point word holding the lane's 4 columns at bit (l & 1) * 16
-  u32x2 s;               // 4 fp16 scales
-  u32x4 x[kXLoads];      // this wave's share of the group's activation rows
+  uint32_t zw[Q];        // zero-point words holding the lane's 4 columns at bit (l & 1) * 16
+  u32x2 s[Q];            // 4 fp16 scales per quantisation group
+  u32x4 x[kXLoads];      // this wave's share of the step's activation rows
 };
 
 // Byte offsets of one lane's loads for group 0; group g adds g times the
@@ -63,25 +65,29 @@ struct Frag {
 template <int MT, int WT>
 struct Lanes {
   uint32_t w, z, s;                     // weights (quad 0), zero-point word, scales
-  uint32_t x[Frag<MT, WT>::kXLoads];    // activation chunks
+  uint32_t x[4 * MT / WT];              // activation chunks
   uint32_t wq;                          // weight offset step between quads (4 packed rows)
-  uint32_t gw, gz, gs;                  // per-group strides (activations: 256 bytes)
+  uint32_t gw;                          // weight stride per 128-k step
+  uint32_t gz, gs;                      // zero-point and scale strides per quantisation group
 };
 
 // activation load i of the group (i = 0 .. 4*MT-1): rows 4 i + l/16, k = 8 (l % 16) .. + 7
 __device__ __forceinline__ int xrow_of(int i, int lane) { return 4 * i + (lane >> 4); }
 
-template <int MT, int WT>
-__device__ __forceinline__ void load_group(Frag<MT, WT>& f, const Resources& rs,
+template <int MT, int WT, int Q>
+__device__ __forceinline__ void load_group(Frag<MT, WT, Q>& f, const Resources& rs,
                                            const Lanes<MT, WT>& o, int g, bool valid) {
   const uint32_t gg = (uint32_t)g;
 #pragma unroll
   for (int it = 0; it < 4; ++it)
     f.w[it] = ld_x4<kNT>(rs.w, o.w + it * o.wq + (valid ? gg * o.gw : kNoLoad));
-  f.zw = ld_x1(rs.z, o.z + (valid ? gg * o.gz : kNoLoad));
-  f.s = ld_x2(rs.s, o.s + (valid ? gg * o.gs : kNoLoad));
 #pragma unroll
-  for (int q = 0; q < Frag<MT, WT>::kXLoads; ++q)
+  for (int q = 0; q < Q; ++q) {
+    f.zw[q] = ld_x1(rs.z, o.z + (valid ? (gg * Q + q) * o.gz : kNoLoad));
+    f.s[q] = ld_x2(rs.s, o.s + (valid ? (gg * Q + q) * o.gs : kNoLoad));
+  }
+#pragma unroll
+  for (int q = 0; q < Frag<MT, WT, Q>::kXLoads; ++q)
     f.x[q] = ld_x4(rs.x, o.x[q] + (valid ? gg * (uint32_t)(kGroup * 2) : kNoLoad));
 }
 
@@ -94,7 +100,7 @@ __device__ __forceinline__ void store_row4(_Float16* dst, float a0, float a1, fl
 
 // SB: split-K partials the last block of a tile loads per batch (one round
 // trip to memory per batch; loads past the last split are masked off)
-template <int MT, int WT, int WK, int D, int SB>
+template <int MT, int WT, int WK, int D, int SB, int Q>
 __global__ __launch_bounds__(64 * WT * WK) void w4a16_skinny_kernel(GemmArgs a, int splits,
                                                                     unsigned* tickets,
                                                                     float* partials) {
@@ -151,7 +157,7 @@ __global__ __launch_bounds__(64 * WT * WK) void w4a16_skinny_kernel(GemmArgs a, 
   o.s = (uint32_t)col * 2;
   o.gs = N * 2;
 #pragma unroll
-  for (int q = 0; q < Frag<MT, WT>::kXLoads; ++q) {
+  for (int q = 0; q < Frag<MT, WT, Q>::kXLoads; ++q) {
     int m = mbase + xrow_of(q * WT + wt, lane);
     m = m < a.M ? m : a.M - 1;                      // rows past M: never stored
     o.x[q] = ((uint32_t)m * (uint32_t)a.ldx + chunk * 8) * 2;
@@ -159,13 +165,13 @@ __global__ __launch_bounds__(64 * WT * WK) void w4a16_skinny_kernel(GemmArgs a, 
   const uint32_t magic = in_vgpr(0x64006400u);
   const int zshift = (lane & 1) * 16;
 
-  Frag<MT, WT> f[D];
+  Frag<MT, WT, Q> f[D];
   auto group_of = [&](int j) { return g0 + (j < n ? j : (n > 0 ? n - 1 : 0)); };
   // prologue loads in the loop's order (f[0] complete, then f[1], ...): the
   // wait counts at the loop head are then the same on entry and on the back edge
 #pragma unroll
   for (int i = 0; i < D; ++i) {
-    load_group<MT, WT>(f[i], rs, o, group_of(i), i < n);
+    load_group<MT, WT, Q>(f[i], rs, o, group_of(i), i < n);
     __builtin_amdgcn_sched_barrier(0);
   }
 
@@ -182,50 +188,55 @@ __global__ __launch_bounds__(64 * WT * WK) void w4a16_skinny_kernel(GemmArgs a, 
     // k order of the dequantised nibbles, into the LDS tile
     uint32_t* xt = xtile(j & 1, wk);
 #pragma unroll
-    for (int q = 0; q < Frag<MT, WT>::kXLoads; ++q)
+    for (int q = 0; q < Frag<MT, WT, Q>::kXLoads; ++q)
       *reinterpret_cast<f16x8*>(xt + xrow_of(q * WT + wt, lane) * kXRowWords + chunk * 4) =
           permute_for_int4(f[i].x[q]);
     lds_barrier();
     if (j < n) {                                  // wave-uniform
-      ZeroPair zz[4];
+      // per quantisation group: exact fp16 (q - z) operands, the group's
+      // fp32 sum over its 128 / Q k, then its scale once
 #pragma unroll
-      for (int c = 0; c < 4; ++c) zz[c] = zero_pair((f[i].zw >> (zshift + 4 * c)) & 0xFu);
-      f32x4 tmp[MT][4];
+      for (int q = 0; q < Q; ++q) {
+        ZeroPair zz[4];
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int c = 0; c < 4; ++c) tmp[mt][c] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int it = 0; it < 4; ++it) {
-        // A layout: row l % 16, k = 32 it + 8 (l / 16) .. + 7
-        f16x8 av[MT];
+        for (int c = 0; c < 4; ++c) zz[c] = zero_pair((f[i].zw[q] >> (zshift + 4 * c)) & 0xFu);
+        f32x4 tmp[MT][4];
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
-          av[mt] = *reinterpret_cast<const f16x8*>(xt + (mt * 16 + chunk) * kXRowWords +
-                                                   (it * 4 + kb) * 4);
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const f16x8 b = dequant_int4_word(f[i].w[it][c], zz[c], magic);
+          for (int c = 0; c < 4; ++c) tmp[mt][c] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int mt = 0; mt < MT; ++mt) tmp[mt][c] = mfma16x16x32(av[mt], b, tmp[mt][c]);
+        for (int it = q * (4 / Q); it < (q + 1) * (4 / Q); ++it) {
+          // A layout: row l % 16, k = 32 it + 8 (l / 16) .. + 7
+          f16x8 av[MT];
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt)
+            av[mt] = *reinterpret_cast<const f16x8*>(xt + (mt * 16 + chunk) * kXRowWords +
+                                                     (it * 4 + kb) * 4);
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            const f16x8 b = dequant_int4_word(f[i].w[it][c], zz[c], magic);
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) tmp[mt][c] = mfma16x16x32(av[mt], b, tmp[mt][c]);
+          }
         }
+        // copy the vector elements to scalars before the bit casts: a bit
+        // cast of an ext-vector element expression reads element 0 with
+        // this compiler
+        const uint32_t s_lo = f[i].s[q].x, s_hi = f[i].s[q].y;
+        const f16x2 s01 = __builtin_bit_cast(f16x2, s_lo);
+        const f16x2 s23 = __builtin_bit_cast(f16x2, s_hi);
+        const float sc[4] = {(float)s01.x, (float)s01.y, (float)s23.x, (float)s23.y};
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+          for (int c = 0; c < 4; ++c)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              acc[mt][c][r] = __builtin_fmaf(sc[c], tmp[mt][c][r], acc[mt][c][r]);
       }
-      // copy the vector elements to scalars before the bit casts: a bit
-      // cast of an ext-vector element expression reads element 0 with
-      // this compiler
-      const uint32_t s_lo = f[i].s.x, s_hi = f[i].s.y;
-      const f16x2 s01 = __builtin_bit_cast(f16x2, s_lo);
-      const f16x2 s23 = __builtin_bit_cast(f16x2, s_hi);
-      const float sc[4] = {(float)s01.x, (float)s01.y, (float)s23.x, (float)s23.y};
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int c = 0; c < 4; ++c)
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            acc[mt][c][r] = __builtin_fmaf(sc[c], tmp[mt][c][r], acc[mt][c][r]);
     }
-    load_group<MT, WT>(f[i], rs, o, group_of(j + D), j + D < n);
+    load_group<MT, WT, Q>(f[i], rs, o, group_of(j + D), j + D < n);
   };
   int j0 = 0;
   for (; j0 + D <= nmax; j0 += D) {
@@ -347,33 +358,21 @@ __global__ __launch_bounds__(64 * WT * WK) void w4a16_skinny_kernel(GemmArgs a, 
   }
 }
 
-template <int MT, int WT, int WK, int D, int SB>
+template <int MT, int WT, int WK, int D, int SB, int Q>
 void launch_t(const GemmArgs& a, const GemmPlan& p, unsigned* tickets, float* partials,
               hipStream_t stream) {
-  hipLaunchKernelGGL((w4a16_skinny_kernel<MT, WT, WK, D, SB>), dim3(p.col_blocks, p.splits, p.mblocks),
-                     dim3(64 * WT * WK), 0, stream, a, p.splits, tickets, partials);
+  hipLaunchKernelGGL((w4a16_skinny_kernel<MT, WT, WK, D, SB, Q>),
+                     dim3(p.col_blocks, p.splits, p.mblocks), dim3(64 * WT * WK), 0, stream, a,
+                     p.splits, tickets, partials);
 }
 
-template <int MT, int WT, int WK>
-void launch_wk(const GemmArgs& a, const GemmPlan& p, unsigned* tickets, float* partials,
-               hipStream_t stream) {
-  // three groups in flight per wave; one batch of partial loads up to 8 splits
-  if (p.splits <= 8) launch_t<MT, WT, WK, 3, 8>(a, p, tickets, partials, stream);
-  else launch_t<MT, WT, WK, 3, 16>(a, p, tickets, partials, stream);
-}
-
-template <int MT>
-void launch_mt(const GemmArgs& a, const GemmPlan& p, unsigned* tickets, float* partials,
-               hipStream_t stream) {
-  switch (p.wt * 16 + p.wk) {
-    case 4 * 16 + 1: launch_wk<MT, 4, 1>(a, p, tickets, partials, stream); break;
-    case 2 * 16 + 2: launch_wk<MT, 2, 2>(a, p, tickets, partials, stream); break;
-    case 1 * 16 + 4: launch_wk<MT, 1, 4>(a, p, tickets, partials, stream); break;
-    case 8 * 16 + 1: launch_wk<MT, 8, 1>(a, p, tickets, partials, stream); break;
-    case 4 * 16 + 2: launch_wk<MT, 4, 2>(a, p, tickets, partials, stream); break;
-    case 2 * 16 + 4: launch_wk<MT, 2, 4>(a, p, tickets, partials, stream); break;
-    default: launch_wk<MT, 1, 8>(a, p, tickets, partials, stream); break;
-  }
+// Two tiles x two k-slices per block, three steps in flight per wave; one
+// batch of partial loads up to 8 splits, batches of 16 beyond.
+template <int MT, int Q>
+void launch_q(const GemmArgs& a, const GemmPlan& p, unsigned* tickets, float* partials,
+              hipStream_t stream) {
+  if (p.splits <= 8) launch_t<MT, 2, 2, 3, 8, Q>(a, p, tickets, partials, stream);
+  else launch_t<MT, 2, 2, 3, 16, Q>(a, p, tickets, partials, stream);
 }
 
 }  // namespace
@@ -418,8 +417,16 @@ hipError_t launch_w4a16_skinny(const GemmArgs& a, const GemmPlan& p, void* works
     tickets = static_cast<unsigned*>(workspace);
     partials = reinterpret_cast<float*>(static_cast<char*>(workspace) + p.ticket_bytes);
   }
-  if (p.mt == 1) launch_mt<1>(a, p, tickets, partials, stream);
-  else launch_mt<2>(a, p, tickets, partials, stream);
+  if (p.wt != 2 || p.wk != 2 || (a.group_size != 128 && a.group_size != 32))
+    return hipErrorInvalidValue;
+  const bool g32 = a.group_size == 32;
+  if (p.mt == 1) {
+    if (g32) launch_q<1, 4>(a, p, tickets, partials, stream);
+    else launch_q<1, 1>(a, p, tickets, partials, stream);
+  } else {
+    if (g32) launch_q<2, 4>(a, p, tickets, partials, stream);
+    else launch_q<2, 1>(a, p, tickets, partials, stream);
+  }
   return hipGetLastError();
 }
 

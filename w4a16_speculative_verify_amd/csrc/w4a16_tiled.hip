@@ -4,16 +4,16 @@
 // prefill compute; at M = 2,048-8,192 rows the W4A16 linear is a dense
 // contraction bound by the matrix cores, not by HBM.
 //
-// Block tile 128 (rows) x 128 (columns), one 128-k quantisation group per
-// K-step, 4 waves as 2 x 2 sub-tiles of 64 x 64 (4 x 4 MFMA 16x16x32 tiles).
+// Block tile 128 (rows) x 128 (columns), 128 k per K-step, 4 waves as 2 x 2 sub-tiles of 64 x 64 (4 x 4 MFMA 16x16x32 tiles).
 //   A (activations): the block's 128 x 128 fp16 slice goes through LDS,
 //     double-buffered, with the k order inside each 8-element block permuted
 //     to match the dequantised nibbles; rows are padded by 16 bytes so the 16
 //     rows of one MFMA operand read fall in different banks.
 //   B (weights): every lane loads its own packed words straight from global
 //     memory (4 columns x 8 k per 128-bit load, the lane layout of the MFMA B
-//     operand), dequantises them in registers exactly (fp16 q - z), and the
-//     group's fp16 scale multiplies the fp32 sum of the group once.
+//     operand), dequantises them in registers exactly (fp16 q - z), and each
+//     quantisation group's fp16 scale multiplies the fp32 sum of the group
+//     once (group size 128, or 32: four groups per K-step).
 //   Weights run two groups ahead in a three-deep register ring, the next
 //   group's activations are requested before the current group's MFMAs; the
 //   per-group barrier orders LDS only, so loads stay in flight across it.
@@ -30,27 +30,34 @@ constexpr int kRowBytes = BK * 2 + 16;            // padded LDS row of A
 constexpr int kRowWords = kRowBytes / 4;
 constexpr int DB = 3;                             // weight groups in flight per lane
 
+// Q quantisation groups per 128-k step (1: group size 128; 4: group size 32)
+template <int Q>
 struct BFrag {
   u32x4 w[4];       // 4 quads of packed rows, 4 columns each
-  uint32_t zw;      // the zero-point word (the lane's 4 columns at zshift)
-  u32x2 s;          // 4 fp16 scales
+  uint32_t zw[Q];   // the zero-point words (the lane's 4 columns at zshift)
+  u32x2 s[Q];       // 4 fp16 scales per quantisation group
 };
 
-// Lane byte offsets of group 0's loads and the per-group strides.
+// Lane byte offsets of step 0's loads; the weight stride per 128-k step, the
+// zero-point and scale strides per quantisation group.
 struct BLanes {
   uint32_t w, wq, gw, z, gz, s, gs;
 };
 
 // Group g's packed words, zero-point word and scales; a group past the last
 // one reads zeros without touching memory (offset pushed past the resource).
-__device__ __forceinline__ void load_b(BFrag& f, const rsrc_t& rw, const rsrc_t& rz,
+template <int Q>
+__device__ __forceinline__ void load_b(BFrag<Q>& f, const rsrc_t& rw, const rsrc_t& rz,
                                        const rsrc_t& rs, const BLanes& o, int g, int G) {
   const uint32_t gg = (uint32_t)(g < G ? g : 0);
   const uint32_t skip = g < G ? 0u : kNoLoad;
 #pragma unroll
   for (int it = 0; it < 4; ++it) f.w[it] = ld_x4<kNT>(rw, (o.w + it * o.wq + gg * o.gw) | skip);
-  f.zw = ld_x1(rz, (o.z + gg * o.gz) | skip);
-  f.s = ld_x2(rs, (o.s + gg * o.gs) | skip);
+#pragma unroll
+  for (int q = 0; q < Q; ++q) {
+    f.zw[q] = ld_x1(rz, (o.z + (gg * Q + q) * o.gz) | skip);
+    f.s[q] = ld_x2(rs, (o.s + (gg * Q + q) * o.gs) | skip);
+  }
 }
 
 // A tile loads: thread t moves 8 consecutive k (16 bytes) of rows t/16 + 16 j.
@@ -75,6 +82,7 @@ __device__ __forceinline__ void store_a(uint32_t* lds, const AFrag& f, int rows_
   }
 }
 
+template <int Q>
 __global__ __launch_bounds__(kThreads) void w4a16_tiled_kernel(GemmArgs a) {
   __shared__ uint32_t As[2][BM * kRowWords];
 
@@ -120,7 +128,7 @@ __global__ __launch_bounds__(kThreads) void w4a16_tiled_kernel(GemmArgs a) {
     for (int c = 0; c < 4; ++c) acc[i][c] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // prologue in the loop's order: weights of groups 0 .. DB-1, then A of group 0
-  BFrag bf[DB];
+  BFrag<Q> bf[DB];
 #pragma unroll
   for (int i = 0; i < DB; ++i) {
     load_b(bf[i], rw, rz, rs, ob, i, G);
@@ -141,47 +149,53 @@ __global__ __launch_bounds__(kThreads) void w4a16_tiled_kernel(GemmArgs a) {
       // the next group's activations, staged into the other LDS buffer below
       load_a(af, rx, oa, g + 1, G);
       if (g < G) {                                  // block-uniform
-        ZeroPair zz[4];
-        {
-          const uint32_t zw = bf[i].zw >> zshift;
-#pragma unroll
-          for (int c = 0; c < 4; ++c) zz[c] = zero_pair((zw >> (4 * c)) & 0xFu);
-        }
-        f32x4 tmp[4][4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-#pragma unroll
-          for (int c = 0; c < 4; ++c) tmp[r][c] = f32x4{0.f, 0.f, 0.f, 0.f};
         const uint32_t* as = As[g & 1];
+        // per quantisation group: exact fp16 (q - z) operands, the group's
+        // fp32 sum over its 128 / Q k, then its scale once
 #pragma unroll
-        for (int it = 0; it < 4; ++it) {
-          f16x8 av[4];
+        for (int q = 0; q < Q; ++q) {
+          ZeroPair zz[4];
+          {
+            const uint32_t zw = bf[i].zw[q] >> zshift;
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int row = wm * 64 + r * 16 + (lane & 15);
-            av[r] = __builtin_bit_cast(
-                f16x8, *reinterpret_cast<const u32x4*>(as + row * kRowWords + it * 16 + kb * 4));
+            for (int c = 0; c < 4; ++c) zz[c] = zero_pair((zw >> (4 * c)) & 0xFu);
           }
+          f32x4 tmp[4][4];
 #pragma unroll
-          for (int c = 0; c < 4; ++c) {
-            const f16x8 bv = dequant_int4_word(bf[i].w[it][c], zz[c], magic);
+          for (int r = 0; r < 4; ++r)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) tmp[r][c] = mfma16x16x32(av[r], bv, tmp[r][c]);
+            for (int c = 0; c < 4; ++c) tmp[r][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int it = q * (4 / Q); it < (q + 1) * (4 / Q); ++it) {
+            f16x8 av[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int row = wm * 64 + r * 16 + (lane & 15);
+              av[r] = __builtin_bit_cast(
+                  f16x8, *reinterpret_cast<const u32x4*>(as + row * kRowWords + it * 16 + kb * 4));
+            }
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+              const f16x8 bv = dequant_int4_word(bf[i].w[it][c], zz[c], magic);
+#pragma unroll
+              for (int r = 0; r < 4; ++r) tmp[r][c] = mfma16x16x32(av[r], bv, tmp[r][c]);
+            }
           }
+          // copy the vector elements to scalars before the bit casts: a bit
+          // cast of an ext-vector element expression reads element 0 with
+          // this compiler
+          const uint32_t s_lo = bf[i].s[q].x, s_hi = bf[i].s[q].y;
+          const f16x2 s01 = __builtin_bit_cast(f16x2, s_lo);
+          const f16x2 s23 = __builtin_bit_cast(f16x2, s_hi);
+          const float sc[4] = {(float)s01.x, (float)s01.y, (float)s23.x, (float)s23.y};
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                acc[r][c][e] = __builtin_fmaf(sc[c], tmp[r][c][e], acc[r][c][e]);
         }
-        // copy the vector elements to scalars before the bit casts: a bit
-        // cast of an ext-vector element expression reads element 0 with
-        // this compiler
-        const uint32_t s_lo = bf[i].s.x, s_hi = bf[i].s.y;
-        const f16x2 s01 = __builtin_bit_cast(f16x2, s_lo);
-        const f16x2 s23 = __builtin_bit_cast(f16x2, s_hi);
-        const float sc[4] = {(float)s01.x, (float)s01.y, (float)s23.x, (float)s23.y};
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-#pragma unroll
-          for (int c = 0; c < 4; ++c)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) acc[r][c][e] = __builtin_fmaf(sc[c], tmp[r][c][e], acc[r][c][e]);
       }
       load_b(bf[i], rw, rz, rs, ob, g + DB, G);
       store_a(As[(g + 1) & 1], af, rows_ok, t);
@@ -209,7 +223,10 @@ __global__ __launch_bounds__(kThreads) void w4a16_tiled_kernel(GemmArgs a) {
 
 hipError_t launch_w4a16_tiled(const GemmArgs& a, hipStream_t stream) {
   dim3 grid((a.N + BN - 1) / BN, (a.M + BM - 1) / BM);
-  hipLaunchKernelGGL(w4a16_tiled_kernel, grid, dim3(kThreads), 0, stream, a);
+  if (a.group_size == 32)
+    hipLaunchKernelGGL(w4a16_tiled_kernel<4>, grid, dim3(kThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL(w4a16_tiled_kernel<1>, grid, dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 

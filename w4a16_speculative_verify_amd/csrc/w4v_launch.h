@@ -35,14 +35,15 @@ struct GemmArgs {
   _Float16* y; int64_t ldy;
   int M, N, K;
   float alpha;
+  int group_size;    // 128, or 32 (four quantisation groups per 128-k step)
 };
 
 struct GemmPlan {
   int mt;            // 16-row m-tiles per block (1 or 2)
   int mblocks;       // blocks along M, each 16*mt rows
   int tiles;         // ceil(N / 64)
-  int wt;            // 64-column tiles per block (1, 2, 4 or 8)
-  int wk;            // k-slices per block (wt * wk = 4 or 8 waves)
+  int wt;            // 64-column tiles per block (2)
+  int wk;            // k-slices per block (2)
   int col_blocks;    // ceil(tiles / wt)
   int splits;        // split-K factor across blocks (1 = none)
   int depth;         // groups in flight per wave (3)
@@ -63,8 +64,8 @@ constexpr int kTiledMinRows = 33;
 constexpr int kLibMinRows = 512;
 constexpr size_t kLibWorkspace = 64ull << 20;   // the library GEMM's own scratch
 hipError_t launch_dequant_w4_f16t(const uint32_t* qweight, const _Float16* scales,
-                                  const uint32_t* qzeros, int K, int N, _Float16* wt,
-                                  hipStream_t stream);
+                                  const uint32_t* qzeros, int K, int N, int group_size,
+                                  _Float16* wt, hipStream_t stream);
 // y = alpha * x @ wt^T through the library (wt: fp16 [N x K]); false if the
 // library has no plan for the shape or reports an error before launching.
 bool lib_gemm_f16_tn(const _Float16* x, int64_t ldx, const _Float16* wt, _Float16* y, int64_t ldy,
