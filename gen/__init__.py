@@ -145,6 +145,12 @@ def lmhead_scales(rng, v: int) -> np.ndarray:
     return rng.uniform(0.001, 0.004, size=v).astype(np.float16)
 
 
+def f16_weights(rng, n: int, k: int) -> np.ndarray:
+    """fp16 [n, k] (one row per output, the layout of a dense layer), N(0, 1/k) drawn in
+    fp64 then rounded: a half-precision linear that keeps unit-RMS activations at unit RMS."""
+    return (rng.standard_normal((n, k)) / math.sqrt(k)).astype(np.float16)
+
+
 @dataclass
 class QLinear:
     """Packed W4A16 linear in the canonical layout (g = group size)."""

@@ -16,12 +16,15 @@ Sources (organisers' page "Efficient LLM Challenge Results", adaptfm.gitlab.io):
                 Table 3 and the paragraph on n-gram drafting: the prompt-
                 lookup drafter copies spans from the prompt, no auxiliary
                 model, fixed K (23 for the team that used it).
-  section 5  -- W4A16 (group size 128), W8A16 lm_head.
+  section 5  -- W4A16 (group size 128), W8A16 lm_head; team #5's target:
+                W4A16 with group size 32, the first two and last two layers
+                and the lm_head in half precision.
 
 Modules:
   quant   -- int4 unpacking and group dequantisation
-  gemm    -- the W4A16 linear and fp16 storage rounding
-  lmhead  -- 8-bit lm_head logits, argmax with tie-break, top-2 margin
+  gemm    -- the W4A16 linear (group size 128 or 32), the fp16 linear, fp16
+             storage rounding
+  lmhead  -- 8-bit and fp16 lm_head logits, argmax with tie-break, top-2 margin
   verify  -- greedy prefix acceptance with sentinels, verified-token count
   step    -- the free-running verify step (chain of linears, lm_head, verify)
   ngram   -- prompt-lookup drafting and appending the accepted tokens

@@ -32,3 +32,14 @@ def w4a16_gemm_columns(x, qweight, scales, qzeros, cols, alpha: float = 1.0,
 def to_fp16(y64: np.ndarray) -> np.ndarray:
     """fp16 storage point: round-to-nearest-even from fp64."""
     return np.asarray(y64, dtype=np.float64).astype(np.float16)
+
+
+def f16_linear(x, w, alpha: float = 1.0) -> np.ndarray:
+    """fp64 [M, N] = alpha * X64 @ W64^T for fp16 weights W [N, K] (one row per output).
+
+    Results page, section 5: team #5 keeps the first two and last two layers
+    of its group-size-32 target in half precision; those linears are plain
+    fp16 products, W in the [out, in] layout of a dense layer.
+    """
+    return alpha * (np.asarray(x).astype(np.float64) @ np.asarray(w).astype(np.float64).T)
+

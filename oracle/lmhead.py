@@ -47,3 +47,22 @@ def argmax_margin(lg: np.ndarray):
 def lmhead_argmax(h, w8, s8):
     """(target ids, max logits, margins) for the rows of ``h``."""
     return argmax_margin(logits(h, w8, s8))
+
+
+def logits_f16(h, w16) -> np.ndarray:
+    """fp64 [M, V]: L[m, v] = sum_h H[m, h] * W[v, h] for an fp16 lm_head W [V, H] (team #5
+    keeps its lm_head in half precision, results page section 5; no scale)."""
+    h64 = np.asarray(h).astype(np.float64)
+    w16 = np.asarray(w16)
+    v = w16.shape[0]
+    out = np.empty((h64.shape[0], v), dtype=np.float64)
+    for lo in range(0, v, _CHUNK):
+        hi = min(v, lo + _CHUNK)
+        out[:, lo:hi] = h64 @ w16[lo:hi].astype(np.float64).T
+    return out
+
+
+def lmhead_argmax_f16(h, w16):
+    """(target ids, max logits, margins) for the rows of ``h`` with an fp16 lm_head."""
+    return argmax_margin(logits_f16(h, w16))
+

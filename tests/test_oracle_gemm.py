@@ -138,3 +138,30 @@ def test_brute_force_exact_rationals_group_32():
                 acc += Fraction(float(x[mm, kk])) * sv * (qv - zv)
             exact = Fraction(1.25) * acc
             assert abs(y[mm, nn] - float(exact)) <= 1e-12 * max(1.0, abs(float(exact)))
+
+
+def test_f16_linear_identity_and_one_hot():
+    rng = np.random.default_rng(29)
+    x = gen.activations(rng, 3, 64)
+    eye = np.eye(64, dtype=np.float16)
+    assert np.array_equal(gemm.to_fp16(gemm.f16_linear(x, eye)).view(np.uint16), x.view(np.uint16))
+    w = np.zeros((40, 64), dtype=np.float16)
+    w[17, 9] = np.float16(0.375)                       # output 17 reads input 9
+    y = gemm.f16_linear(x, w, alpha=2.0)
+    expect = np.zeros((3, 40))
+    expect[:, 17] = 0.75 * x[:, 9].astype(np.float64)
+    assert np.array_equal(y, expect)
+
+
+def test_f16_linear_brute_force_exact_rationals():
+    rng = np.random.default_rng(31)
+    m, k, n = 2, 48, 5
+    x = gen.activations(rng, m, k)
+    w = gen.f16_weights(rng, n, k)
+    y = gemm.f16_linear(x, w, alpha=0.5)
+    for mm in range(m):
+        for nn in range(n):
+            exact = Fraction(1, 2) * sum(Fraction(float(x[mm, kk])) * Fraction(float(w[nn, kk]))
+                                         for kk in range(k))
+            assert abs(y[mm, nn] - float(exact)) <= 1e-13 * max(1.0, abs(float(exact)))
+    assert w.dtype == np.float16 and w.shape == (n, k)

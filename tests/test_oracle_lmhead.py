@@ -91,3 +91,34 @@ def test_chunking_boundary_is_seamless():
     for vv in (0, lmhead._CHUNK - 1, lmhead._CHUNK, v - 1):
         direct = (hid.astype(np.float64) @ w8[vv].astype(np.float64)) * float(s8[vv])
         assert np.allclose(lg[:, vv], direct, rtol=1e-15, atol=0)
+
+
+def test_f16_one_hot_hidden_and_brute_force():
+    rng = np.random.default_rng(41)
+    v, h = 30, 40
+    w = gen.f16_weights(rng, v, h)
+    hid = np.zeros((2, h), dtype=np.float16)
+    hid[0, 7] = 1.0
+    hid[1, 39] = -2.0
+    lg = lmhead.logits_f16(hid, w)
+    assert np.array_equal(lg[0], w[:, 7].astype(np.float64))
+    assert np.array_equal(lg[1], -2.0 * w[:, 39].astype(np.float64))
+    x = gen.activations(rng, 2, h)
+    lg = lmhead.logits_f16(x, w)
+    for mm in range(2):
+        for vv in range(v):
+            exact = sum(Fraction(float(x[mm, kk])) * Fraction(float(w[vv, kk])) for kk in range(h))
+            assert abs(lg[mm, vv] - float(exact)) <= 1e-13 * max(1.0, abs(float(exact)))
+
+
+def test_f16_planted_winner_across_the_chunk_seam():
+    # rows on both sides of the 8192-row slice boundary; the winner sits right after it
+    rng = np.random.default_rng(43)
+    v, h = 8192 + 100, 16
+    w = np.zeros((v, h), dtype=np.float16)
+    w[8191, 3] = np.float16(0.5)
+    w[8192, 3] = np.float16(0.625)
+    hid = np.zeros((1, h), dtype=np.float16)
+    hid[0, 3] = 2.0
+    t, top, margin = lmhead.lmhead_argmax_f16(hid, w)
+    assert t[0] == 8192 and top[0] == 1.25 and margin[0] == 0.25
