@@ -172,6 +172,50 @@ int w8a16_lmhead_argmax_verify(const void* h, int64_t ldh,
                                void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * Half-precision parts of a partly quantised target (section 5: team #5
+ * serves a W4A16 group-size-32 target that keeps its first two and last two
+ * layers and its lm_head in fp16).
+ *
+ * fp16 lm_head with fused greedy argmax, optionally the greedy verify:
+ *   logit[m, v] = sum_h h[m, h] * w[v, h]  (fp32, never stored);
+ *   target_ids[m] = argmax_v logit[m, v], ties -> lowest v.
+ * w        fp16 [V x H] row-major (one vocabulary row per output), 16-byte
+ *          aligned; V * H * 2 bytes below 2 GiB (W4V_ERR_UNSUPPORTED).
+ * h, target_ids, max_logits, M, H, workspace: as for w8a16_lmhead_argmax
+ *          (same workspace size: f16_lmhead_argmax_workspace_size).
+ * B == 0   argmax only (draft_ids, accepted_len, out_tokens ignored).
+ * B > 0    M must equal B * (K + 1) (W4V_ERR_INVALID_ARG otherwise); then the
+ *          greedy prefix acceptance of w8a16_lmhead_argmax_verify runs in the
+ *          same launch.
+ * ---------------------------------------------------------------------- */
+size_t f16_lmhead_argmax_workspace_size(int M, int H, int V);
+
+int f16_lmhead_argmax_verify(const void* h, int64_t ldh, const void* w,
+                             int32_t* target_ids, float* max_logits, int M, int H, int V,
+                             const int32_t* draft_ids, int B, int K,
+                             int32_t* accepted_len, int32_t* out_tokens,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+/* fp16 linear: y[m, n] = fp16_rne( alpha * sum_k x[m, k] * w[n, k] ), fp32
+ * accumulation, computed by the vendor library's plain fp16 GEMM.
+ * x        fp16 [M x K], row stride ldx >= K; w fp16 [N x K] (one row per
+ *          output, the layout of a dense layer), row stride ldw >= K;
+ *          y fp16 [M x N] out, row stride ldy >= N.  All 16-byte aligned,
+ *          strides multiples of 8; y must overlap neither x nor w.
+ * workspace  f16_gemm_workspace_size(M, N, K) bytes, 256-byte aligned: the
+ *          library GEMM's scratch after the first 64 KiB + 4 MiB, which are
+ *          left alone (the split-K counters and partials of w4a16_gemm), so
+ *          one workspace serves both kinds of linear on a stream.
+ * Errors   W4V_ERR_UNSUPPORTED when the library has no plan for the shape
+ *          or fails before launching; there is no other path.
+ * ---------------------------------------------------------------------- */
+size_t f16_gemm_workspace_size(int M, int N, int K);
+
+int f16_gemm(const void* x, int64_t ldx, const void* w, int64_t ldw, void* y, int64_t ldy,
+             int M, int N, int K, float alpha, void* workspace, size_t workspace_bytes,
+             void* stream);
+
+/* ------------------------------------------------------------------------
  * A chain of W4A16 linears in one launch (section 3: the target's forward
  * pass over the verify block -- every linear of every layer -- at M <= 16
  * rows).  Linear l reads the leading K_l columns of linear l-1's output

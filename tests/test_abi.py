@@ -212,3 +212,59 @@ def test_append_accepted_validation(lib, kw, status):
     a.update(kw)
     st = lib.append_accepted(a["h"], a["ld"], a["lens"], a["B"], a["K"], a["out"], a["acc"], None)
     assert st == status
+
+
+def f16lm(lib, h=A, ldh=2560, w=A, t=A, ml=None, M=16, H=2560, V=4096, d=None, B=0, K=0,
+          acc=None, out=None, ws=A * 256, wsb=1 << 30):
+    return lib.f16_lmhead_argmax_verify(h, ldh, w, t, ml, M, H, V, d, B, K, acc, out, ws, wsb, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(H=100, ldh=128), INVALID),
+    (dict(h=None), INVALID),
+    (dict(w=None), INVALID),
+    (dict(t=None), INVALID),
+    (dict(w=A + 8), ALIGN),
+    (dict(ml=A + 2), ALIGN),
+    (dict(ws=None, wsb=0), WORKSPACE),
+    (dict(M=0), OK),
+    (dict(B=-1), INVALID),
+    (dict(B=2, K=15), INVALID),                               # M != B * (K + 1)
+    (dict(M=32, B=2, K=15, d=A, acc=None, out=A), INVALID),   # verify outputs missing
+    (dict(M=32, B=2, K=15, d=A, acc=A + 2, out=A), ALIGN),
+    (dict(H=1 << 15, ldh=1 << 15, V=1 << 15), UNSUPPORTED),  # 2 GiB of fp16 weights
+])
+def test_f16_lmhead_validation(lib, kw, status):
+    assert f16lm(lib, **kw) == status
+
+
+def f16g(lib, x=A, ldx=2560, w=A * 32, ldw=2560, y=A * 1024, ldy=2560, M=16, N=2560, K=2560,
+         ws=A * 256, wsb=1 << 30):
+    return lib.f16_gemm(x, ldx, w, ldw, y, ldy, M, N, K, ctypes.c_float(1.0), ws, wsb, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(K=0), INVALID),
+    (dict(M=-1), INVALID),
+    (dict(x=None), INVALID),
+    (dict(w=None), INVALID),
+    (dict(ldx=2000), INVALID),
+    (dict(ldw=2000), INVALID),
+    (dict(ldy=2000), INVALID),
+    (dict(x=A + 2), ALIGN),
+    (dict(ldw=2564), ALIGN),
+    (dict(y=A * 32 + 64), INVALID),              # y overlaps w
+    (dict(y=A + 64), INVALID),                   # y overlaps x
+    (dict(ws=None, wsb=0), WORKSPACE),
+    (dict(wsb=1 << 20), WORKSPACE),
+    (dict(M=0), OK),
+    (dict(N=0, ldy=0), OK),
+])
+def test_f16_gemm_validation(lib, kw, status):
+    assert f16g(lib, **kw) == status
+
+
+def test_f16_workspace_sizes(lib):
+    assert w4v.f16_gemm_workspace_size(16, 2560, 2560) >= 1 << 20
+    assert w4v.f16_gemm_workspace_size(0, 2560, 2560) == 0
+    assert lib.f16_lmhead_argmax_workspace_size(16, 2560, 151936) == w4v.lmhead_workspace_size(16, 2560, 151936)

@@ -48,6 +48,12 @@ SIGNATURES = {
     "append_accepted": (_int, [_vp, _i64, _vp, _int, _int, _vp, _vp, _vp]),
     "w8a16_lmhead_argmax_verify": (_int, [_vp, _i64, _vp, _vp, _vp, _vp, _int, _int, _vp, _int,
                                           _int, _vp, _vp, _vp, _sz, _vp]),
+    "f16_lmhead_argmax_workspace_size": (_sz, [_int, _int, _int]),
+    "f16_lmhead_argmax_verify": (_int, [_vp, _i64, _vp, _vp, _vp, _int, _int, _int, _vp, _int,
+                                        _int, _vp, _vp, _vp, _sz, _vp]),
+    "f16_gemm_workspace_size": (_sz, [_int, _int, _int]),
+    "f16_gemm": (_int, [_vp, _i64, _vp, _i64, _vp, _i64, _int, _int, _int, ctypes.c_float, _vp,
+                        _sz, _vp]),
 }
 
 
@@ -260,6 +266,71 @@ def w8a16_lmhead_argmax_verify(h, w, scales, draft_ids, target_ids=None, max_log
         _ptr(workspace), wbytes, _stream(stream))
     _check(st, "w8a16_lmhead_argmax_verify")
     return target_ids, max_logits, accepted_len, out_tokens
+
+
+def f16_lmhead_argmax_verify(h, w, draft_ids=None, target_ids=None, max_logits=None,
+                             accepted_len=None, out_tokens=None, want_max=True, workspace=None,
+                             stream=None):
+    """fp16 lm_head (w fp16 [V, H]) + argmax, and the greedy verify when ``draft_ids``
+    (int32 [B, K]) is given (then h has B*(K+1) rows).
+
+    Returns (target_ids [M], max_logits or None, accepted_len [B] or None, out_tokens or None).
+    """
+    torch = _require(h, __import__("torch").float16, "h")
+    _require(w, torch.float16, "w")
+    m, hdim, v = h.shape[0], w.shape[1], w.shape[0]
+    dev = h.device
+    b = k = 0
+    if draft_ids is not None:
+        _require(draft_ids, torch.int32, "draft_ids")
+        b, k = draft_ids.shape
+        if m != b * (k + 1):
+            raise ValueError(f"h has {m} rows, B*(K+1) = {b * (k + 1)}")
+        if not draft_ids.is_contiguous():
+            raise ValueError("draft_ids must be contiguous")
+        if accepted_len is None:
+            accepted_len = torch.empty(b, dtype=torch.int32, device=dev)
+        if out_tokens is None:
+            out_tokens = torch.empty((b, k + 1), dtype=torch.int32, device=dev)
+    if target_ids is None:
+        target_ids = torch.empty(m, dtype=torch.int32, device=dev)
+    if want_max and max_logits is None:
+        max_logits = torch.empty(m, dtype=torch.float32, device=dev)
+    need = int(load().f16_lmhead_argmax_workspace_size(m, hdim, v))
+    if workspace is None and need > 0:
+        workspace = new_workspace(need, dev)
+    wbytes = workspace.numel() if workspace is not None else 0
+    st = load().f16_lmhead_argmax_verify(
+        _ptr(h), h.stride(0), _ptr(w), _ptr(target_ids), _ptr(max_logits), m, hdim, v,
+        _ptr(draft_ids) if k > 0 else None, b, k, _ptr(accepted_len), _ptr(out_tokens),
+        _ptr(workspace), wbytes, _stream(stream))
+    _check(st, "f16_lmhead_argmax_verify")
+    return target_ids, max_logits, accepted_len, out_tokens
+
+
+def f16_gemm_workspace_size(m: int, n: int, k: int) -> int:
+    return int(load().f16_gemm_workspace_size(m, n, k))
+
+
+def f16_gemm(x, w, alpha: float = 1.0, out=None, workspace=None, stream=None):
+    """y[M, N] = fp16(alpha * x[:, :K] @ w.T) for fp16 w [N, K] (vendor library GEMM)."""
+    torch = _require(x, __import__("torch").float16, "x")
+    _require(w, torch.float16, "w")
+    n, k = w.shape
+    m = x.shape[0]
+    if x.shape[1] < k:
+        raise ValueError(f"x has {x.shape[1]} columns, the weights need {k}")
+    if out is None:
+        out = torch.empty((m, n), dtype=torch.float16, device=x.device)
+    _require(out, torch.float16, "out")
+    need = f16_gemm_workspace_size(m, n, k)
+    if workspace is None and need > 0:
+        workspace = new_workspace(need, x.device)
+    wbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = load().f16_gemm(_ptr(x), x.stride(0), _ptr(w), w.stride(0), _ptr(out), out.stride(0), m,
+                         n, k, ctypes.c_float(alpha), _ptr(workspace), wbytes, _stream(stream))
+    _check(st, "f16_gemm")
+    return out
 
 
 # ------------------------------------------------------------------- chain of linears

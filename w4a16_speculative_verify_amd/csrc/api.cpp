@@ -68,7 +68,7 @@ int workspace_check(size_t need, const void* ws, size_t ws_bytes) {
   return W4V_OK;
 }
 
-int run_lmhead(const void* h, int64_t ldh, const int8_t* w, const void* scales,
+int run_lmhead(const void* h, int64_t ldh, const void* w, const void* scales, int f16,
                int32_t* target_ids, float* max_logits, int M, int H, int V,
                const int32_t* draft_ids, int B, int K, int32_t* accepted_len,
                int32_t* out_tokens, void* workspace, size_t workspace_bytes, void* stream) {
@@ -81,6 +81,7 @@ int run_lmhead(const void* h, int64_t ldh, const int8_t* w, const void* scales,
   a.ldh = ldh;
   a.w = w;
   a.scales = static_cast<const _Float16*>(scales);
+  a.f16 = f16;
   a.target_ids = target_ids;
   a.max_logits = max_logits;
   a.M = M;
@@ -297,7 +298,7 @@ int w4a16_gemm(const void* x, int64_t ldx, const int32_t* qweight, const void* s
     hipError_t e = w4v::launch_dequant_w4_f16t(a.qweight, a.scales, a.qzeros, K, N, group_size,
                                                wt, s);
     if (e != hipSuccess) return W4V_ERR_HIP;
-    if (w4v::lib_gemm_f16_tn(a.x, ldx, wt, a.y, ldy, M, N, K, alpha,
+    if (w4v::lib_gemm_f16_tn(a.x, ldx, wt, K, a.y, ldy, M, N, K, alpha,
                              base + lib_weights_bytes(N, K), w4v::kLibWorkspace, s))
       return W4V_OK;
     if (big) return W4V_ERR_HIP;
@@ -317,7 +318,7 @@ int w8a16_lmhead_argmax(const void* h, int64_t ldh, const int8_t* w, const void*
   int st = lmhead_check(h, ldh, w, scales, target_ids, M, H, V);
   if (st != W4V_OK || M == 0) return st;
   if (max_logits && !aligned(max_logits, 4)) return W4V_ERR_ALIGNMENT;
-  return run_lmhead(h, ldh, w, scales, target_ids, max_logits, M, H, V, nullptr, 0, 0, nullptr,
+  return run_lmhead(h, ldh, w, scales, 0, target_ids, max_logits, M, H, V, nullptr, 0, 0, nullptr,
                     nullptr, workspace, workspace_bytes, stream);
 }
 
@@ -350,8 +351,64 @@ int w8a16_lmhead_argmax_verify(const void* h, int64_t ldh, const int8_t* w, cons
   if ((max_logits && !aligned(max_logits, 4)) || !aligned(accepted_len, 4) ||
       !aligned(out_tokens, 4) || (draft_ids && !aligned(draft_ids, 4)))
     return W4V_ERR_ALIGNMENT;
-  return run_lmhead(h, ldh, w, scales, target_ids, max_logits, M, H, V, draft_ids, B, K,
+  return run_lmhead(h, ldh, w, scales, 0, target_ids, max_logits, M, H, V, draft_ids, B, K,
                     accepted_len, out_tokens, workspace, workspace_bytes, stream);
+}
+
+size_t f16_lmhead_argmax_workspace_size(int M, int H, int V) {
+  return w8a16_lmhead_argmax_workspace_size(M, H, V);
+}
+
+int f16_lmhead_argmax_verify(const void* h, int64_t ldh, const void* w, int32_t* target_ids,
+                             float* max_logits, int M, int H, int V, const int32_t* draft_ids,
+                             int B, int K, int32_t* accepted_len, int32_t* out_tokens,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+  if (B < 0 || K < 0) return W4V_ERR_INVALID_ARG;
+  if (B > 0 && (long long)B * (K + 1) != (long long)M) return W4V_ERR_INVALID_ARG;
+  // the fp16 head reads no scales: any non-null, aligned pointer passes the shared check
+  int st = lmhead_check(h, ldh, static_cast<const int8_t*>(w), w, target_ids, M, H, V);
+  if (st != W4V_OK || M == 0) return st;
+  if ((size_t)V * (size_t)H * 2 >= (1ull << 31)) return W4V_ERR_UNSUPPORTED;
+  if (B > 0 && (!accepted_len || !out_tokens || (K > 0 && !draft_ids))) return W4V_ERR_INVALID_ARG;
+  if ((max_logits && !aligned(max_logits, 4)) ||
+      (B > 0 && (!aligned(accepted_len, 4) || !aligned(out_tokens, 4) ||
+                 (draft_ids && !aligned(draft_ids, 4)))))
+    return W4V_ERR_ALIGNMENT;
+  return run_lmhead(h, ldh, w, nullptr, 1, target_ids, max_logits, M, H, V,
+                    B > 0 ? draft_ids : nullptr, B, B > 0 ? K : 0, B > 0 ? accepted_len : nullptr,
+                    B > 0 ? out_tokens : nullptr, workspace, workspace_bytes, stream);
+}
+
+// The library's scratch follows the counter prefix and the partials region,
+// as for the W4A16 library path, so that one workspace serves both kinds of
+// linear on a stream.
+size_t f16_gemm_workspace_size(int M, int N, int K) {
+  if (M <= 0 || N <= 0 || K <= 0) return 0;
+  return lib_offset() + w4v::kLibWorkspace;
+}
+
+int f16_gemm(const void* x, int64_t ldx, const void* w, int64_t ldw, void* y, int64_t ldy, int M,
+             int N, int K, float alpha, void* workspace, size_t workspace_bytes, void* stream) {
+  if (M < 0 || N < 0 || K <= 0) return W4V_ERR_INVALID_ARG;
+  if (M == 0 || N == 0) return W4V_OK;
+  if (!x || !w || !y) return W4V_ERR_INVALID_ARG;
+  if (ldx < K || ldw < K || ldy < N) return W4V_ERR_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(w, 16) || !aligned(y, 16) || ldx % 8 != 0 || ldw % 8 != 0 ||
+      ldy % 8 != 0)
+    return W4V_ERR_ALIGNMENT;
+  const size_t xbytes = ((size_t)(M - 1) * (size_t)ldx + (size_t)K) * 2;
+  const size_t ybytes = ((size_t)(M - 1) * (size_t)ldy + (size_t)N) * 2;
+  const size_t wbytes = ((size_t)(N - 1) * (size_t)ldw + (size_t)K) * 2;
+  if (ranges_overlap(x, xbytes, y, ybytes) || ranges_overlap(w, wbytes, y, ybytes))
+    return W4V_ERR_INVALID_ARG;
+  int st = workspace_check(f16_gemm_workspace_size(M, N, K), workspace, workspace_bytes);
+  if (st != W4V_OK) return st;
+  if (!w4v::lib_gemm_f16_tn(static_cast<const _Float16*>(x), ldx, static_cast<const _Float16*>(w),
+                            ldw, static_cast<_Float16*>(y), ldy, M, N, K, alpha,
+                            static_cast<char*>(workspace) + lib_offset(),
+                            workspace_bytes - lib_offset(), static_cast<hipStream_t>(stream)))
+    return W4V_ERR_UNSUPPORTED;
+  return W4V_OK;
 }
 
 int ngram_draft(const int32_t* history, int64_t ld, const int32_t* lengths, int B, int n_max,

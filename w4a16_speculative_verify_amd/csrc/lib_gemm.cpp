@@ -1,9 +1,10 @@
-// Plain fp16 GEMM through hipBLASLt for the prefill-shaped W4A16 linear
-// (after the weights were dequantised by this library's own kernel).
+// Plain fp16 GEMM through hipBLASLt: the prefill-shaped W4A16 linear (after
+// the weights were dequantised by this library's own kernel) and the
+// half-precision linears of a partly quantised target.
 //
-//   y[M x N] (row-major, ldy) = alpha * x[M x K] (row-major, ldx) @ wt[N x K]^T
+//   y[M x N] (row-major, ldy) = alpha * x[M x K] (row-major, ldx) @ wt[N x K]^T (ldw)
 //
-// In the library's column-major terms: D^T[N x M] = op_T(wt as K x N, ld K) x
+// In the library's column-major terms: D^T[N x M] = op_T(wt as K x N, ld ldw) x
 // op_N(x as K x M, ld ldx), fp32 accumulation, fp32 alpha, fp16 in and out.
 // One handle per device and one matmul plan per shape are created on first
 // use and kept for the life of the process.
@@ -21,7 +22,7 @@ namespace {
 
 struct Plan {
   int dev, M, N, K;
-  int64_t ldx, ldy;
+  int64_t ldx, ldy, ldw;
   hipblasLtMatmulDesc_t op;
   hipblasLtMatrixLayout_t la, lb, lc;
   hipblasLtMatmulAlgo_t algo;
@@ -43,19 +44,19 @@ hipblasLtHandle_t handle_for(int dev) {
 
 // The plan for a shape, made once (nullptr if the library offers none).
 const Plan* plan_for(hipblasLtHandle_t h, int dev, int M, int N, int K, int64_t ldx, int64_t ldy,
-                     size_t scratch_bytes) {
+                     int64_t ldw, size_t scratch_bytes) {
   for (auto& p : g_plans)
     if (p.dev == dev && p.M == M && p.N == N && p.K == K && p.ldx == ldx && p.ldy == ldy &&
-        p.ws <= scratch_bytes)
+        p.ldw == ldw && p.ws <= scratch_bytes)
       return &p;
   Plan p{};
-  p.dev = dev; p.M = M; p.N = N; p.K = K; p.ldx = ldx; p.ldy = ldy;
+  p.dev = dev; p.M = M; p.N = N; p.K = K; p.ldx = ldx; p.ldy = ldy; p.ldw = ldw;
   if (hipblasLtMatmulDescCreate(&p.op, HIPBLAS_COMPUTE_32F, HIP_R_32F) != HIPBLAS_STATUS_SUCCESS)
     return nullptr;
   const hipblasOperation_t ta = HIPBLAS_OP_T, tb = HIPBLAS_OP_N;
   hipblasLtMatmulDescSetAttribute(p.op, HIPBLASLT_MATMUL_DESC_TRANSA, &ta, sizeof(ta));
   hipblasLtMatmulDescSetAttribute(p.op, HIPBLASLT_MATMUL_DESC_TRANSB, &tb, sizeof(tb));
-  bool ok = hipblasLtMatrixLayoutCreate(&p.la, HIP_R_16F, (uint64_t)K, (uint64_t)N, K) ==
+  bool ok = hipblasLtMatrixLayoutCreate(&p.la, HIP_R_16F, (uint64_t)K, (uint64_t)N, ldw) ==
                 HIPBLAS_STATUS_SUCCESS &&
             hipblasLtMatrixLayoutCreate(&p.lb, HIP_R_16F, (uint64_t)K, (uint64_t)M, ldx) ==
                 HIPBLAS_STATUS_SUCCESS &&
@@ -96,15 +97,15 @@ const Plan* plan_for(hipblasLtHandle_t h, int dev, int M, int N, int K, int64_t 
 
 }  // namespace
 
-bool lib_gemm_f16_tn(const _Float16* x, int64_t ldx, const _Float16* wt, _Float16* y, int64_t ldy,
-                     int M, int N, int K, float alpha, void* scratch, size_t scratch_bytes,
-                     hipStream_t stream) {
+bool lib_gemm_f16_tn(const _Float16* x, int64_t ldx, const _Float16* wt, int64_t ldw, _Float16* y,
+                     int64_t ldy, int M, int N, int K, float alpha, void* scratch,
+                     size_t scratch_bytes, hipStream_t stream) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return false;
   std::lock_guard<std::mutex> lock(g_mu);
   hipblasLtHandle_t h = handle_for(dev);
   if (!h) return false;
-  const Plan* p = plan_for(h, dev, M, N, K, ldx, ldy, scratch_bytes);
+  const Plan* p = plan_for(h, dev, M, N, K, ldx, ldy, ldw, scratch_bytes);
   if (!p) return false;
   const float beta = 0.f;
   return hipblasLtMatmul(h, p->op, &alpha, wt, p->la, x, p->lb, &beta, y, p->lc, y, p->lc,

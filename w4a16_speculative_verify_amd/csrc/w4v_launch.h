@@ -66,16 +66,19 @@ constexpr size_t kLibWorkspace = 64ull << 20;   // the library GEMM's own scratc
 hipError_t launch_dequant_w4_f16t(const uint32_t* qweight, const _Float16* scales,
                                   const uint32_t* qzeros, int K, int N, int group_size,
                                   _Float16* wt, hipStream_t stream);
-// y = alpha * x @ wt^T through the library (wt: fp16 [N x K]); false if the
-// library has no plan for the shape or reports an error before launching.
-bool lib_gemm_f16_tn(const _Float16* x, int64_t ldx, const _Float16* wt, _Float16* y, int64_t ldy,
-                     int M, int N, int K, float alpha, void* scratch, size_t scratch_bytes,
-                     hipStream_t stream);
+// y = alpha * x @ wt^T through the library (wt: fp16 [N x K], row stride
+// ldw); false if the library has no plan for the shape or reports an error
+// before launching.
+bool lib_gemm_f16_tn(const _Float16* x, int64_t ldx, const _Float16* wt, int64_t ldw, _Float16* y,
+                     int64_t ldy, int M, int N, int K, float alpha, void* scratch,
+                     size_t scratch_bytes, hipStream_t stream);
 
 // ---------------------------------------------------------------- lm_head
 struct LmheadArgs {
   const _Float16* h; int64_t ldh;
-  const int8_t* w; const _Float16* scales;
+  const void* w;         // int8 [V x H] with fp16 scales [V], or fp16 [V x H] (scales NULL)
+  const _Float16* scales;
+  int f16;               // 1: fp16 weights, no scales
   int32_t* target_ids; float* max_logits;
   int M, H, V;
   // fused greedy verify (draft_ids may be NULL when K == 0; B == 0 disables it)
@@ -86,8 +89,8 @@ struct LmheadArgs {
 struct LmheadPlan {
   int mt;            // 16-row m-tiles per block (1 or 2)
   int mblocks;
-  int tiles;         // 16-row vocabulary tiles per wave pass (1, 2 or 4)
-  int depth;         // steps in flight per wave (3, 4, 6 or 8)
+  int tiles;         // 16-row vocabulary tiles per wave pass (1 or 2)
+  int depth;         // steps in flight per wave (3)
   int vblocks;       // blocks along the vocabulary
   size_t ticket_bytes;
   size_t partial_bytes;

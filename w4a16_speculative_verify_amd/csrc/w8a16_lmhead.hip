@@ -6,7 +6,9 @@
 //   wave pass = TILES x 16 vocabulary rows over the whole hidden width H, in
 //     steps of 128 k.  Lane l streams 32 consecutive bytes (k = 32*(l/16) ..)
 //     of row v0 + 16*t + l%16 per step: two 128-bit loads per tile.  Each
-//     8-byte slice is the B operand of one 16x16x32 MFMA.
+//     8-byte slice is the B operand of one 16x16x32 MFMA.  With fp16 weights
+//     (a half-precision head) the lane streams 64 bytes, four 128-bit loads,
+//     each the B operand of one MFMA as loaded.
 //   A (hidden rows) = one 128-k chunk per step, loaded once per block (one
 //     16-byte load per thread) into a double-buffered LDS tile that the four
 //     waves share: per-wave loads of it would cost a CU as much load
@@ -47,14 +49,17 @@ __device__ __forceinline__ void shfl_best(float& v, int& i, int mask) {
   }
 }
 
-template <int MT, int TILES>
+// F16 = 0: int8 weights with one fp16 scale per vocabulary row; F16 = 1: fp16
+// weights, no scale (a half-precision lm_head, results page section 5).
+template <int MT, int TILES, int F16>
 struct Step {
-  u32x4 w[TILES][2];     // 32 bytes of each tile row
-  u32x4 h[MT];           // this thread's 16 bytes of the hidden chunk
-  uint32_t sc[TILES];    // fp16 scale of each tile row (loaded with a pass's last step)
+  static constexpr int kLoads = F16 ? 4 : 2;      // 128-bit loads per tile row (32 k)
+  u32x4 w[TILES][kLoads];  // 32 k of each tile row
+  u32x4 h[MT];             // this thread's 16 bytes of the hidden chunk
+  uint32_t sc[TILES];      // fp16 scale of each tile row (int8 only; with a pass's last step)
 };
 
-template <int MT, int TILES, int D>
+template <int MT, int TILES, int D, int F16>
 __global__ __launch_bounds__(kThreads) void lmhead_argmax_kernel(LmheadArgs a, unsigned* ticket,
                                                                  float* pval, int* pidx) {
   const int lane = threadIdx.x & 63;
@@ -90,7 +95,8 @@ __global__ __launch_bounds__(kThreads) void lmhead_argmax_kernel(LmheadArgs a, u
     return vb0 + pass * kRowsPerPass + wave * TILES * 16 + 16 * t + (lane & 15);
   };
 
-  auto load_step = [&](Step<MT, TILES>& f, int st) {
+  constexpr int EB = F16 ? 2 : 1;                   // bytes per weight
+  auto load_step = [&](Step<MT, TILES, F16>& f, int st) {
     // Offsets are masked by OR-ing kNoLoad (bit 31) in, never by choosing
     // between two loads: the compiler turns a select on a block-uniform
     // condition into a branch around the load.
@@ -101,21 +107,25 @@ __global__ __launch_bounds__(kThreads) void lmhead_argmax_kernel(LmheadArgs a, u
 #pragma unroll
     for (int t = 0; t < TILES; ++t) {
       const int v = row_of(pass, t);
-      const uint32_t off = ((uint32_t)(v < vb1 ? v : 0) * (uint32_t)a.H + kb * 32 + ch * kChunk) |
-                           skip | (v < vb1 ? 0u : kNoLoad);
-      f.w[t][0] = ld_x4(rw, off);
-      f.w[t][1] = ld_x4(rw, off + 16);
+      const uint32_t off =
+          (((uint32_t)(v < vb1 ? v : 0) * (uint32_t)a.H + kb * 32 + ch * kChunk) * EB) | skip |
+          (v < vb1 ? 0u : kNoLoad);
+#pragma unroll
+      for (int u = 0; u < Step<MT, TILES, F16>::kLoads; ++u) f.w[t][u] = ld_x4(rw, off + 16 * u);
     }
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) f.h[mt] = ld_x4(rh, (hoff[mt] + ch * kChunk * 2) | skip);
     // the row scales ride with the last step of a pass (a load at the pass end
     // would wait for the whole ring)
-    const uint32_t not_last = ch == nchunks - 1 ? 0u : kNoLoad;
+    if constexpr (!F16) {
+      const uint32_t not_last = ch == nchunks - 1 ? 0u : kNoLoad;
 #pragma unroll
-    for (int t = 0; t < TILES; ++t) {
-      const int v = row_of(pass, t);
-      f.sc[t] = __builtin_amdgcn_raw_buffer_load_b16(
-          rs, ((uint32_t)(v < vb1 ? v : 0) * 2) | skip | not_last | (v < vb1 ? 0u : kNoLoad), 0, 0);
+      for (int t = 0; t < TILES; ++t) {
+        const int v = row_of(pass, t);
+        f.sc[t] = __builtin_amdgcn_raw_buffer_load_b16(
+            rs, ((uint32_t)(v < vb1 ? v : 0) * 2) | skip | not_last | (v < vb1 ? 0u : kNoLoad), 0,
+            0);
+      }
     }
   };
 
@@ -134,7 +144,7 @@ __global__ __launch_bounds__(kThreads) void lmhead_argmax_kernel(LmheadArgs a, u
 #pragma unroll
     for (int t = 0; t < TILES; ++t) acc[mt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  Step<MT, TILES> f[D];
+  Step<MT, TILES, F16> f[D];
   // prologue in the loop's order, so the loop head's wait counts agree on entry
 #pragma unroll
   for (int i = 0; i < D; ++i) {
@@ -163,9 +173,14 @@ __global__ __launch_bounds__(kThreads) void lmhead_argmax_kernel(LmheadArgs a, u
                                                      kb * 16 + q * 4);
 #pragma unroll
           for (int t = 0; t < TILES; ++t) {
-            const u32x4& src = f[i].w[t][q >> 1];
-            const u32x2 d = (q & 1) ? u32x2{src.z, src.w} : u32x2{src.x, src.y};
-            const f16x8 b = dequant_int8_x8(d);
+            f16x8 b;
+            if constexpr (F16) {
+              b = __builtin_bit_cast(f16x8, f[i].w[t][q]);
+            } else {
+              const u32x4& src = f[i].w[t][q >> 1];
+              const u32x2 d = (q & 1) ? u32x2{src.z, src.w} : u32x2{src.x, src.y};
+              b = dequant_int8_x8(d);
+            }
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) acc[mt][t] = mfma16x16x32(av[mt], b, acc[mt][t]);
           }
@@ -176,8 +191,8 @@ __global__ __launch_bounds__(kThreads) void lmhead_argmax_kernel(LmheadArgs a, u
           for (int t = 0; t < TILES; ++t) {
             const int v = row_of(pass, t);
             if (v < vb1) {
-              const uint32_t sbits = f[i].sc[t];
-              const float sv = (float)__builtin_bit_cast(_Float16, (uint16_t)sbits);
+              float sv = 1.f;
+              if constexpr (!F16) sv = (float)__builtin_bit_cast(_Float16, (uint16_t)f[i].sc[t]);
 #pragma unroll
               for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
@@ -282,24 +297,12 @@ __global__ __launch_bounds__(kThreads) void lmhead_argmax_kernel(LmheadArgs a, u
 template <int MT, int TILES>
 void launch_t(const LmheadArgs& a, const LmheadPlan& p, unsigned* ticket, float* pval, int* pidx,
               hipStream_t stream) {
-  switch (p.depth) {
-    case 3:
-      hipLaunchKernelGGL((lmhead_argmax_kernel<MT, TILES, 3>), dim3(p.vblocks, p.mblocks),
-                         dim3(kThreads), 0, stream, a, ticket, pval, pidx);
-      break;
-    case 4:
-      hipLaunchKernelGGL((lmhead_argmax_kernel<MT, TILES, 4>), dim3(p.vblocks, p.mblocks),
-                         dim3(kThreads), 0, stream, a, ticket, pval, pidx);
-      break;
-    case 6:
-      hipLaunchKernelGGL((lmhead_argmax_kernel<MT, TILES, 6>), dim3(p.vblocks, p.mblocks),
-                         dim3(kThreads), 0, stream, a, ticket, pval, pidx);
-      break;
-    default:
-      hipLaunchKernelGGL((lmhead_argmax_kernel<MT, TILES, 8>), dim3(p.vblocks, p.mblocks),
-                         dim3(kThreads), 0, stream, a, ticket, pval, pidx);
-      break;
-  }
+  if (a.f16)
+    hipLaunchKernelGGL((lmhead_argmax_kernel<MT, TILES, 3, 1>), dim3(p.vblocks, p.mblocks),
+                       dim3(kThreads), 0, stream, a, ticket, pval, pidx);
+  else
+    hipLaunchKernelGGL((lmhead_argmax_kernel<MT, TILES, 3, 0>), dim3(p.vblocks, p.mblocks),
+                       dim3(kThreads), 0, stream, a, ticket, pval, pidx);
 }
 
 }  // namespace
@@ -333,13 +336,12 @@ hipError_t launch_lmhead_argmax(const LmheadArgs& a, const LmheadPlan& p, void* 
   float* pval = reinterpret_cast<float*>(base);
   int* pidx = reinterpret_cast<int*>(base + align_up(nblocks * 16 * p.mt * sizeof(float),
                                                      kWorkspaceAlign));
+  if (p.depth != 3 || (p.tiles != 1 && p.tiles != 2)) return hipErrorInvalidValue;
   if (p.mt == 1) {
-    if (p.tiles == 4) launch_t<1, 4>(a, p, ticket, pval, pidx, stream);
-    else if (p.tiles == 2) launch_t<1, 2>(a, p, ticket, pval, pidx, stream);
+    if (p.tiles == 2) launch_t<1, 2>(a, p, ticket, pval, pidx, stream);
     else launch_t<1, 1>(a, p, ticket, pval, pidx, stream);
   } else {
-    if (p.tiles == 4) launch_t<2, 4>(a, p, ticket, pval, pidx, stream);
-    else if (p.tiles == 2) launch_t<2, 2>(a, p, ticket, pval, pidx, stream);
+    if (p.tiles == 2) launch_t<2, 2>(a, p, ticket, pval, pidx, stream);
     else launch_t<2, 1>(a, p, ticket, pval, pidx, stream);
   }
   return hipGetLastError();
