@@ -18,8 +18,9 @@ on the stream it runs on.  ``cpu_baseline`` times the numpy oracle on a
 bounded sample of the same workload on the host cores.  ``prefill`` (the
 M = 2048 / 8192 linears), ``drafter`` (prompt-lookup drafting over
 8192-token histories, the step before the verify) and ``drafter_int4_step``
-(a 4-bit drafter's 21 linears at M = 16) are timed after the step, outside
-its timed region.
+(a 4-bit drafter's 21 linears at M = 16) and ``g32_target_step`` (a target
+quantised with group size 32, fp16 first and last layers and lm_head, K = 23)
+are timed after the step, outside its timed region.
 """
 from __future__ import annotations
 
@@ -185,6 +186,78 @@ def drafter_gemm(dev, reps: int = 20):
             "gbs": round(gbs, 1), "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2)}
 
 
+def g32_target(dev, steps: int = 50, warmup: int = 5):
+    """A verify step of team #5's target: 36 layers of the 4B-class linears, W4A16 with
+    group size 32 except layers 0, 1, 34 and 35 in fp16 (vendor library GEMM), an fp16
+    lm_head 2560 -> 151936 with fused argmax and greedy verify, at K = 23 (24 rows).
+    Drafts accept min(23, Geometric(0.25)) tokens against the step's own target ids."""
+    import numpy as np
+    import torch
+
+    import gen
+    from w4a16_speculative_verify_amd.step import DeviceLinear, VerifyStep
+
+    tg = gen.make_g32_target()
+    up = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    lins, nbytes = [], 0
+    m = tg.m
+    for l in tg.linears:
+        if l.w16 is not None:
+            lins.append(DeviceLinear(None, None, None, l.k, l.n, l.alpha, w16=up(l.w16)))
+            nbytes += l.n * l.k * 2
+        else:
+            lins.append(DeviceLinear(up(l.q.qweight), up(l.q.scales), up(l.q.qzeros), l.k, l.n,
+                                     l.alpha, group_size=gen.G32_GROUP))
+            g = l.k // gen.G32_GROUP
+            nbytes += l.k * l.n // 2 + g * l.n * 2 + g * (l.n // 8) * 4
+        nbytes += m * l.k * 2 + m * l.n * 2
+    v = tg.lm_w16.shape[0]
+    nbytes += v * gen.HIDDEN * 2 + m * gen.HIDDEN * 2 + m * 4 + tg.k_draft * 4 + m * 4 + 4
+    step = VerifyStep(lins, up(tg.lm_w16), None, m, 1, tg.k_draft, device=dev)
+    x = up(tg.x)
+    no_drafts = torch.full((1, tg.k_draft), -1, dtype=torch.int32, device=dev)
+    t_host = step(x, no_drafts)[0].cpu().numpy()
+    rng = np.random.default_rng(2323)
+    total = warmup + steps
+    drafts = np.stack([gen.drafts_with_prefix(rng, t_host, tg.k_draft, v,
+                                              gen.draw_r_geometric(rng, tg.k_draft))
+                       for _ in range(total)])[:, None, :]
+    drafts_dev = up(drafts.astype(np.int32))
+    buf = torch.empty((1, tg.k_draft), dtype=torch.int32, device=dev)
+    acc_hist = torch.zeros(total, dtype=torch.int32, device=dev)
+    step(x, buf)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step(x, buf)
+
+    def one(i):
+        buf.copy_(drafts_dev[i], non_blocking=True)
+        g.replay()
+        acc_hist[i:i + 1].copy_(step.accepted_len, non_blocking=True)
+
+    for i in range(warmup):
+        one(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(warmup, total):
+        one(i)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    tokens = int(acc_hist[warmup:].sum().item()) + steps
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    del g, step, lins
+    torch.cuda.empty_cache()
+    return {"workload": "36 layers x 4B-class linears, W4A16 g32 with layers 0, 1, 34, 35 in fp16, "
+                        "fp16 lm_head 2560->151936 + argmax + greedy verify, K=23 (M=24)",
+            "m": m, "k_draft": tg.k_draft, "ms_per_step": round(ms, 4), "step_bytes": nbytes,
+            "gbs": round(gbs, 1), "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+            "verified_tokens_per_s": round(tokens / (ms * 1e-3 * steps), 1),
+            "mean_accepted_plus_one": round(tokens / steps, 3)}
+
+
 def drafter(dev, reps: int = 200):
     """Prompt-lookup drafting ahead of the verify (not part of the timed step):
     ngram_draft over B synthetic histories of 8192 tokens (half copied spans),
@@ -238,6 +311,8 @@ def main():
                     help="skip the prefill-shaped (M = 2048 / 8192) GEMM timing")
     ap.add_argument("--no-drafter", action="store_true",
                     help="skip the drafter timings (prompt lookup, 4-bit drafter step)")
+    ap.add_argument("--no-g32", action="store_true",
+                    help="skip the group-size-32 target step (fp16 first and last layers)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="one device-to-device copy of this many MiB before timing (counter calibration)")
@@ -365,6 +440,12 @@ def main():
         del g_step, g_lin
         pre = prefill(dev)
 
+    g32 = None
+    if not args.no_g32:
+        print("[bench] timing the group-size-32 target step (generating its weights)",
+              file=sys.stderr, flush=True)
+        g32 = g32_target(dev)
+
     dgemm = None
     if not args.no_drafter:
         print("[bench] timing the 4-bit drafter step", file=sys.stderr, flush=True)
@@ -416,6 +497,7 @@ def main():
         "prefill": pre,
         "drafter": draft,
         "drafter_int4_step": dgemm,
+        "g32_target_step": g32,
     }
     print(json.dumps(out), flush=True)
 

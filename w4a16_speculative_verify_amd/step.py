@@ -17,18 +17,21 @@ from dataclasses import dataclass
 
 import torch
 
-from . import (Chain, gemm_workspace_size, lmhead_workspace_size, new_workspace, w4a16_gemm,
+from . import (Chain, f16_gemm, f16_gemm_workspace_size, f16_lmhead_argmax_verify,
+               gemm_workspace_size, lmhead_workspace_size, new_workspace, w4a16_gemm,
                w8a16_lmhead_argmax_verify)
 
 
 @dataclass
 class DeviceLinear:
-    qweight: torch.Tensor   # int32 [k/8, n]
-    scales: torch.Tensor    # fp16 [k/128, n]
-    qzeros: torch.Tensor    # int32 [k/128, n/8]
+    qweight: torch.Tensor | None   # int32 [k/8, n]
+    scales: torch.Tensor | None    # fp16 [k/g, n]
+    qzeros: torch.Tensor | None    # int32 [k/g, n/8]
     k_in: int
     n_out: int
     alpha: float
+    group_size: int = 128
+    w16: torch.Tensor | None = None   # fp16 [n, k]: a half-precision linear instead
 
 
 class VerifyStep:
@@ -51,7 +54,9 @@ class VerifyStep:
         for i in range(1, len(self.out)):
             if self.out[i].data_ptr() == self.out[i - 1].data_ptr():
                 raise ValueError("consecutive linears would share a buffer")
-        need = max([gemm_workspace_size(m, l.n_out, l.k_in) for l in self.linears] + [0])
+        need = max([f16_gemm_workspace_size(m, l.n_out, l.k_in) if l.w16 is not None
+                    else gemm_workspace_size(m, l.n_out, l.k_in, l.group_size)
+                    for l in self.linears] + [0])
         if lm_w is not None:
             need = max(need, lmhead_workspace_size(m, lm_w.shape[1], lm_w.shape[0]))
         self.workspace = new_workspace(need, dev)
@@ -73,13 +78,22 @@ class VerifyStep:
             return self.chain(x, out=self.out[-1])
         h = x
         for lin, y in zip(self.linears, self.out):
-            w4a16_gemm(h[:, :lin.k_in], lin.qweight, lin.scales, lin.qzeros, alpha=lin.alpha,
-                       out=y, workspace=self.workspace)
+            if lin.w16 is not None:
+                f16_gemm(h[:, :lin.k_in], lin.w16, alpha=lin.alpha, out=y, workspace=self.workspace)
+            else:
+                w4a16_gemm(h[:, :lin.k_in], lin.qweight, lin.scales, lin.qzeros, alpha=lin.alpha,
+                           out=y, workspace=self.workspace, group_size=lin.group_size)
             h = y
         return h
 
     def head(self, h: torch.Tensor, drafts: torch.Tensor):
-        """Fused lm_head + argmax + greedy verify on the final hidden rows."""
+        """Fused lm_head + argmax + greedy verify on the final hidden rows (an fp16 lm_head
+        when no scales are given)."""
+        if self.lm_s is None:
+            return f16_lmhead_argmax_verify(h, self.lm_w, drafts, target_ids=self.target_ids,
+                                            max_logits=self.max_logits,
+                                            accepted_len=self.accepted_len,
+                                            out_tokens=self.out_tokens, workspace=self.workspace)
         return w8a16_lmhead_argmax_verify(h, self.lm_w, self.lm_s, drafts,
                                           target_ids=self.target_ids, max_logits=self.max_logits,
                                           accepted_len=self.accepted_len,
