@@ -432,6 +432,30 @@ def make_g32_target(seed_offset: int = 0, layers: int = 36, vocab: int = VOCAB,
     return MixedTarget(x, lins, lm, m, m - 1)
 
 
+# ---------------------------------------------------------------- recurrent state commit
+# Inputs of a Gated DeltaNet state commit (the state the next verify block
+# starts from, driven by the accepted length): a committed state per head and
+# the block's per-position keys, values and gates.  Keys have unit length (the
+# layer normalises them), the decay gate alpha ~ U[0.9, 1), the write
+# strength beta ~ U[0, 1), values and the state N(0, 1).  The pages name the
+# layer type (results page, hazards: most of the target's layers are Gated
+# DeltaNet) but not its sizes: 128-wide keys and values per head.
+GDN_DK = 128
+GDN_DV = 128
+
+
+def gdn_inputs(rng, b: int, t: int, h: int, dk: int = GDN_DK, dv: int = GDN_DV):
+    """(state fp32 [b, h, dv, dk], k fp32 [b, t, h, dk], v fp32 [b, t, h, dv],
+    alpha fp32 [b, t, h], beta fp32 [b, t, h]), drawn in that order."""
+    state = rng.standard_normal((b, h, dv, dk)).astype(np.float32)
+    k = rng.standard_normal((b, t, h, dk))
+    k = (k / np.linalg.norm(k, axis=-1, keepdims=True)).astype(np.float32)
+    v = rng.standard_normal((b, t, h, dv)).astype(np.float32)
+    alpha = rng.uniform(0.9, 1.0, size=(b, t, h)).astype(np.float32)
+    beta = rng.uniform(0.0, 1.0, size=(b, t, h)).astype(np.float32)
+    return state, k, v, alpha, beta
+
+
 # ---------------------------------------------------------------- drafting inputs
 # Token histories for the prompt-lookup drafter ("Efficient LLM Challenge
 # Results", section 3: the n-gram drafter copies spans from the prompt; the

@@ -28,6 +28,7 @@ Modules:
   verify  -- greedy prefix acceptance with sentinels, verified-token count
   step    -- the free-running verify step (chain of linears, lm_head, verify)
   ngram   -- prompt-lookup drafting and appending the accepted tokens
+  gdn     -- committing a Gated DeltaNet state to the accepted prefix
 
 Every function is pinned by a ``-m "not gpu"`` test (pack/unpack round trips,
 hand-built words, identity and one-hot weights, closed forms, exact-rational
@@ -35,4 +36,4 @@ brute force on tiny shapes, exhaustive enumeration for the verify and the
 drafter).  No
 function here is "parity unpinned".
 """
-from . import quant, gemm, lmhead, verify, step, ngram  # noqa: F401
+from . import quant, gemm, lmhead, verify, step, ngram, gdn  # noqa: F401
