@@ -18,9 +18,11 @@ on the stream it runs on.  ``cpu_baseline`` times the numpy oracle on a
 bounded sample of the same workload on the host cores.  ``prefill`` (the
 M = 2048 / 8192 linears), ``drafter`` (prompt-lookup drafting over
 8192-token histories, the step before the verify) and ``drafter_int4_step``
-(a 4-bit drafter's 21 linears at M = 16) and ``g32_target_step`` (a target
+(a 4-bit drafter's 21 linears at M = 16), ``g32_target_step`` (a target
 quantised with group size 32, fp16 first and last layers and lm_head, K = 23)
-are timed after the step, outside its timed region.
+and ``gdn_state_commit`` (recurrent states advanced by the accepted prefix,
+the step after the verify) are timed after the step, outside its timed
+region.
 """
 from __future__ import annotations
 
@@ -258,6 +260,50 @@ def g32_target(dev, steps: int = 50, warmup: int = 5):
             "mean_accepted_plus_one": round(tokens / steps, 3)}
 
 
+def gdn_commit(dev, reps: int = 20):
+    """Committing Gated DeltaNet states to the accepted prefix after a verify at K = 15:
+    27 recurrent layers (three of every four of the 36) x 16 heads of 128 x 128 fp32 state,
+    all committed in one launch; B = 1 and 8 sequences with min(15, Geometric(0.25)) accepted
+    drafts.  Average of ``reps`` launches replayed from a HIP graph; algorithmic bytes are the
+    states read and written plus the accepted positions' keys, values and gates."""
+    import numpy as np
+    import torch
+
+    import gen
+    import w4a16_speculative_verify_amd as w4v
+
+    layers, heads, d, t = 27, 16, gen.GDN_DK, 16
+    h = layers * heads
+    out = {"layers": layers, "heads_per_layer": heads, "head_dim": d, "positions": t}
+    for b in (1, 8):
+        rng = np.random.default_rng(4100 + b)
+        S, k, v, al, be = gen.gdn_inputs(rng, b, t, h, d, d)
+        acc = np.array([gen.draw_r_geometric(rng, t - 1) for _ in range(b)], np.int32)
+        up = lambda a: torch.from_numpy(a).to(dev)
+        s_d, k_d, v_d, al_d, be_d, acc_d = (up(a) for a in (S, k, v, al, be, acc))
+        w4v.gdn_state_commit(s_d, k_d, v_d, al_d, be_d, acc_d)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(reps):
+                w4v.gdn_state_commit(s_d, k_d, v_d, al_d, be_d, acc_d)
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / reps
+        nbytes = int(b * h * 2 * d * d * 4 + int((acc + 1).sum()) * h * (2 * d + 2) * 4 + b * 4)
+        gbs = nbytes / (us * 1e-6) / 1e9
+        out[f"b{b}"] = {"us": round(us, 2), "bytes": nbytes, "gbs": round(gbs, 1),
+                        "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+                        "accepted": acc.tolist()}
+        del g, s_d, k_d, v_d
+    return out
+
+
 def drafter(dev, reps: int = 200):
     """Prompt-lookup drafting ahead of the verify (not part of the timed step):
     ngram_draft over B synthetic histories of 8192 tokens (half copied spans),
@@ -310,7 +356,8 @@ def main():
     ap.add_argument("--no-prefill", action="store_true",
                     help="skip the prefill-shaped (M = 2048 / 8192) GEMM timing")
     ap.add_argument("--no-drafter", action="store_true",
-                    help="skip the drafter timings (prompt lookup, 4-bit drafter step)")
+                    help="skip the timings of the steps around the verify (prompt lookup, "
+                         "4-bit drafter step, recurrent-state commit)")
     ap.add_argument("--no-g32", action="store_true",
                     help="skip the group-size-32 target step (fp16 first and last layers)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -440,6 +487,11 @@ def main():
         del g_step, g_lin
         pre = prefill(dev)
 
+    commit = None
+    if not args.no_drafter:
+        print("[bench] timing the recurrent-state commit", file=sys.stderr, flush=True)
+        commit = gdn_commit(dev)
+
     g32 = None
     if not args.no_g32:
         print("[bench] timing the group-size-32 target step (generating its weights)",
@@ -498,6 +550,7 @@ def main():
         "drafter": draft,
         "drafter_int4_step": dgemm,
         "g32_target_step": g32,
+        "gdn_state_commit": commit,
     }
     print(json.dumps(out), flush=True)
 

@@ -216,6 +216,29 @@ int f16_gemm(const void* x, int64_t ldx, const void* w, int64_t ldw, void* y, in
              void* stream);
 
 /* ------------------------------------------------------------------------
+ * Committing a Gated DeltaNet state to the verify's accepted prefix (results
+ * page, hazards list: rejected drafts corrupted the recurrent state of the
+ * target's Gated DeltaNet layers; section 3: the runner-up's constant-K fix).
+ * The state committed before the verify block is advanced by exactly the
+ * accepted positions -- position 0 (the last committed token) and the a_b
+ * accepted drafts -- a_b + 1 steps of the gated delta rule:
+ *   S <- alpha_t * S (I - beta_t k_t k_t^T) + beta_t v_t k_t^T
+ * Rejected positions are never applied.
+ * state    fp32 [B x H x D x D] in/out (S[b, h] is [dv x dk] row-major),
+ *          16-byte aligned.  H counts heads over all layers committed together.
+ * k, v     fp32 [B x T x H x D]: the block's keys (unit length in the layer)
+ *          and values at positions 0 .. T-1; 4-byte aligned; must not overlap
+ *          the state.
+ * alpha, beta  fp32 [B x T x H]: decay gate and write strength.
+ * accepted_len int32 [B] (e.g. greedy_verify's output), clamped to [0, T-1].
+ * Sizes    B >= 0 (0: nothing to do), T in 1..32, D 64 or 128
+ *          (W4V_ERR_UNSUPPORTED otherwise), B*T*H*D*4 bytes below 2 GiB.
+ * ---------------------------------------------------------------------- */
+int gdn_state_commit(float* state, const float* k, const float* v, const float* alpha,
+                     const float* beta, const int32_t* accepted_len, int B, int T, int H, int D,
+                     void* stream);
+
+/* ------------------------------------------------------------------------
  * A chain of W4A16 linears in one launch (section 3: the target's forward
  * pass over the verify block -- every linear of every layer -- at M <= 16
  * rows).  Linear l reads the leading K_l columns of linear l-1's output

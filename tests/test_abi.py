@@ -268,3 +268,25 @@ def test_f16_workspace_sizes(lib):
     assert w4v.f16_gemm_workspace_size(16, 2560, 2560) >= 1 << 20
     assert w4v.f16_gemm_workspace_size(0, 2560, 2560) == 0
     assert lib.f16_lmhead_argmax_workspace_size(16, 2560, 151936) == w4v.lmhead_workspace_size(16, 2560, 151936)
+
+
+def gdnc(lib, s=A * 256, k=A, v=A * 2, al=A * 3, be=A * 4, acc=A * 5, B=2, T=16, H=4, D=128):
+    return lib.gdn_state_commit(s, k, v, al, be, acc, B, T, H, D, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=-1), INVALID),
+    (dict(T=0), INVALID),
+    (dict(H=0), INVALID),
+    (dict(T=33), UNSUPPORTED),
+    (dict(D=96), UNSUPPORTED),
+    (dict(B=0), OK),
+    (dict(s=None), INVALID),
+    (dict(acc=None), INVALID),
+    (dict(s=A * 256 + 4), ALIGN),
+    (dict(be=A * 4 + 2), ALIGN),
+    (dict(k=A * 256 + 64), INVALID),             # keys overlap the state
+    (dict(B=4096, T=32, H=64), UNSUPPORTED),     # keys of 2 GiB or more
+])
+def test_gdn_commit_validation(lib, kw, status):
+    assert gdnc(lib, **kw) == status

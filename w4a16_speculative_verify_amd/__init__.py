@@ -51,6 +51,7 @@ SIGNATURES = {
     "f16_lmhead_argmax_workspace_size": (_sz, [_int, _int, _int]),
     "f16_lmhead_argmax_verify": (_int, [_vp, _i64, _vp, _vp, _vp, _int, _int, _int, _vp, _int,
                                         _int, _vp, _vp, _vp, _sz, _vp]),
+    "gdn_state_commit": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _int, _int, _int, _int, _vp]),
     "f16_gemm_workspace_size": (_sz, [_int, _int, _int]),
     "f16_gemm": (_int, [_vp, _i64, _vp, _i64, _vp, _i64, _int, _int, _int, ctypes.c_float, _vp,
                         _sz, _vp]),
@@ -306,6 +307,29 @@ def f16_lmhead_argmax_verify(h, w, draft_ids=None, target_ids=None, max_logits=N
         _ptr(workspace), wbytes, _stream(stream))
     _check(st, "f16_lmhead_argmax_verify")
     return target_ids, max_logits, accepted_len, out_tokens
+
+
+def gdn_state_commit(state, k, v, alpha, beta, accepted_len, stream=None):
+    """Advance state fp32 [B, H, D, D] (in place) by the accepted positions 0 .. a_b of the
+    block: k, v fp32 [B, T, H, D], alpha, beta fp32 [B, T, H], accepted_len int32 [B]."""
+    torch = _require(state, __import__("torch").float32, "state")
+    for t, name in ((k, "k"), (v, "v"), (alpha, "alpha"), (beta, "beta")):
+        _require(t, torch.float32, name)
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    _require(accepted_len, torch.int32, "accepted_len")
+    if not state.is_contiguous():
+        raise ValueError("state must be contiguous")
+    b, h, d, d2 = state.shape
+    t = k.shape[1]
+    if d != d2 or tuple(k.shape) != (b, t, h, d) or tuple(v.shape) != (b, t, h, d) or \
+            tuple(alpha.shape) != (b, t, h) or tuple(beta.shape) != (b, t, h) or \
+            tuple(accepted_len.shape) != (b,):
+        raise ValueError("gdn_state_commit: shapes do not match state [B, H, D, D]")
+    st = load().gdn_state_commit(_ptr(state), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
+                                 _ptr(accepted_len), b, t, h, d, _stream(stream))
+    _check(st, "gdn_state_commit")
+    return state
 
 
 def f16_gemm_workspace_size(m: int, n: int, k: int) -> int:

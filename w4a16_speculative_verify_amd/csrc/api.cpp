@@ -411,6 +411,26 @@ int f16_gemm(const void* x, int64_t ldx, const void* w, int64_t ldw, void* y, in
   return W4V_OK;
 }
 
+int gdn_state_commit(float* state, const float* k, const float* v, const float* alpha,
+                     const float* beta, const int32_t* accepted_len, int B, int T, int H, int D,
+                     void* stream) {
+  if (B < 0 || T < 1 || H < 1 || D < 1) return W4V_ERR_INVALID_ARG;
+  if (T > w4v::kGdnMaxT || (D != 64 && D != 128) || B > kMaxGridYZ) return W4V_ERR_UNSUPPORTED;
+  if (B == 0) return W4V_OK;
+  if (!state || !k || !v || !alpha || !beta || !accepted_len) return W4V_ERR_INVALID_ARG;
+  if (!aligned(state, 16) || !aligned(k, 4) || !aligned(v, 4) || !aligned(alpha, 4) ||
+      !aligned(beta, 4) || !aligned(accepted_len, 4))
+    return W4V_ERR_ALIGNMENT;
+  // keys and values are read through buffer resources with 32-bit offsets
+  if ((size_t)B * T * H * D * 4 >= (1ull << 31)) return W4V_ERR_UNSUPPORTED;
+  const size_t sbytes = (size_t)B * H * D * D * 4, kbytes = (size_t)B * T * H * D * 4;
+  if (ranges_overlap(state, sbytes, k, kbytes) || ranges_overlap(state, sbytes, v, kbytes))
+    return W4V_ERR_INVALID_ARG;
+  hipError_t e = w4v::launch_gdn_commit(state, k, v, alpha, beta, accepted_len, B, T, H, D,
+                                        static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? W4V_OK : W4V_ERR_HIP;
+}
+
 int ngram_draft(const int32_t* history, int64_t ld, const int32_t* lengths, int B, int n_max,
                 int n_min, int K, int32_t* drafts, void* stream) {
   if (B < 0 || ld < 1 || K < 1 || n_min < 1 || n_max < n_min) return W4V_ERR_INVALID_ARG;

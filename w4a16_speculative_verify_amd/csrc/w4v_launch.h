@@ -163,6 +163,12 @@ hipError_t launch_append_accepted(int32_t* history, int64_t ld, int32_t* lengths
                                   const int32_t* out_tokens, const int32_t* accepted_len,
                                   hipStream_t stream);
 
+// ---------------------------------------------------------------- recurrent state commit
+constexpr int kGdnMaxT = 32;      // positions of a verify block (K + 1) the commit stages
+hipError_t launch_gdn_commit(float* state, const float* k, const float* v, const float* alpha,
+                             const float* beta, const int32_t* accepted_len, int B, int T, int H,
+                             int D, hipStream_t stream);
+
 // ---------------------------------------------------------------- verify
 hipError_t launch_greedy_verify(const int32_t* target_ids, const int32_t* draft_ids, int B, int K,
                                 int V, int32_t* accepted_len, int32_t* out_tokens,
