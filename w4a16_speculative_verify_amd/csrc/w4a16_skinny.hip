@@ -36,8 +36,6 @@ namespace w4v {
 
 namespace {
 
-constexpr int kMaxWaves = 8;
-
 struct Resources {
   rsrc_t w, z, s, x;
 };
