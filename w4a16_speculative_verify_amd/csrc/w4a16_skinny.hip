@@ -364,13 +364,20 @@ void launch_t(const GemmArgs& a, const GemmPlan& p, unsigned* tickets, float* pa
                      p.splits, tickets, partials);
 }
 
-// Two tiles x two k-slices per block, three steps in flight per wave; one
-// batch of partial loads up to 8 splits, batches of 16 beyond.
+// Four k-slices per block, one or two tiles, three steps in flight per wave;
+// one batch of partial loads up to 8 splits, batches of 16 beyond.
+template <int MT, int WT, int Q>
+void launch_w(const GemmArgs& a, const GemmPlan& p, unsigned* tickets, float* partials,
+              hipStream_t stream) {
+  if (p.splits <= 8) launch_t<MT, WT, 4, 3, 8, Q>(a, p, tickets, partials, stream);
+  else launch_t<MT, WT, 4, 3, 16, Q>(a, p, tickets, partials, stream);
+}
+
 template <int MT, int Q>
 void launch_q(const GemmArgs& a, const GemmPlan& p, unsigned* tickets, float* partials,
               hipStream_t stream) {
-  if (p.splits <= 8) launch_t<MT, 2, 2, 3, 8, Q>(a, p, tickets, partials, stream);
-  else launch_t<MT, 2, 2, 3, 16, Q>(a, p, tickets, partials, stream);
+  if (p.wt == 1) launch_w<MT, 1, Q>(a, p, tickets, partials, stream);
+  else launch_w<MT, 2, Q>(a, p, tickets, partials, stream);
 }
 
 }  // namespace
@@ -382,27 +389,38 @@ GemmPlan plan_w4a16(int M, int N, int K, int num_cus) {
   p.mblocks = (M + rows_blk - 1) / rows_blk;
   p.tiles = (N + kColTile - 1) / kColTile;
   const int G = K / kGroup;
-  // Two tiles x two k-slices per block, and splits for about 192 blocks (3/4
-  // of the CUs: the split-K tail grows with the number of splits), keeping at
-  // least two groups per k-slice.  Measured best or within 5% of the best of
-  // the tile / k-slice / split choices on MI355X for the 4B-class verify
-  // shapes at M = 16 (QKV, O, gate+up, down).
-  p.wt = 2;
-  p.wk = 2;
+  // Four k-slices per block (added through LDS); one 64-column tile per block,
+  // two when the tiles alone outnumber the CUs.  The split-K factor minimises
+  // the steps of the longest wave times the rounds of waves per SIMD, the
+  // fewest splits on ties, with at most two blocks per CU once the groups are
+  // split.  On MI355X this picks the best or near-best of the measured
+  // tile / k-slice / split / depth choices for the 4B-class verify shapes at
+  // M = 16 (QKV 5 splits, O 4, down 5, gate+up 1 with two tiles per block).
+  p.wk = 4;
+  p.wt = ((long)p.tiles * p.mblocks > num_cus) ? 2 : 1;
   p.col_blocks = (p.tiles + p.wt - 1) / p.wt;
+  const long simds = 4L * num_cus;
+  const size_t part_per_split = (size_t)p.mblocks * rows_blk * p.col_blocks * p.wt * kColTile *
+                                sizeof(float);
+  const int smax = ((size_t)p.tiles * p.mblocks <= kMaxTickets) ? G : 1;
   int splits = 1;
-  if ((size_t)p.tiles * p.mblocks <= kMaxTickets) {
-    const long blocks = (long)p.col_blocks * p.mblocks;
-    splits = (int)(192L * num_cus / 256 / blocks);
-    if (splits > G / (2 * p.wk)) splits = G / (2 * p.wk);
-    if (splits < 1) splits = 1;
+  long best = -1;
+  for (int s = 1; s <= smax; ++s) {
+    const long blocks = (long)p.col_blocks * p.mblocks * s;
+    if (s > 1 && (blocks > 2L * num_cus || part_per_split * s > kPartialRegion)) break;
+    const long steps = ((G + s - 1) / s + p.wk - 1) / p.wk;   // of the longest wave
+    const long waves = blocks * p.wt * p.wk;
+    const long cost = steps * ((waves + simds - 1) / simds);
+    if (best < 0 || cost < best) {
+      best = cost;
+      splits = s;
+    }
   }
   p.splits = splits;
   p.depth = 3;
   if (splits > 1) {
     p.ticket_bytes = kTicketRegion;
-    p.partial_bytes = (size_t)p.mblocks * splits * rows_blk * p.col_blocks * p.wt * kColTile *
-                      sizeof(float);
+    p.partial_bytes = part_per_split * splits;
   }
   return p;
 }
@@ -415,7 +433,8 @@ hipError_t launch_w4a16_skinny(const GemmArgs& a, const GemmPlan& p, void* works
     tickets = static_cast<unsigned*>(workspace);
     partials = reinterpret_cast<float*>(static_cast<char*>(workspace) + p.ticket_bytes);
   }
-  if (p.wt != 2 || p.wk != 2 || (a.group_size != 128 && a.group_size != 32))
+  if ((p.wt != 1 && p.wt != 2) || p.wk != 4 || p.depth != 3 ||
+      (a.group_size != 128 && a.group_size != 32))
     return hipErrorInvalidValue;
   const bool g32 = a.group_size == 32;
   if (p.mt == 1) {

@@ -42,8 +42,8 @@ struct GemmPlan {
   int mt;            // 16-row m-tiles per block (1 or 2)
   int mblocks;       // blocks along M, each 16*mt rows
   int tiles;         // ceil(N / 64)
-  int wt;            // 64-column tiles per block (2)
-  int wk;            // k-slices per block (2)
+  int wt;            // 64-column tiles per block (1 or 2)
+  int wk;            // k-slices per block (4)
   int col_blocks;    // ceil(tiles / wt)
   int splits;        // split-K factor across blocks (1 = none)
   int depth;         // groups in flight per wave (3)
