@@ -304,6 +304,120 @@ def gdn_commit(dev, reps: int = 20):
     return out
 
 
+def decode_m1(lins, x16, reps: int = 20):
+    """Plain decode (one activation row) through the 144 linears of the verify-step
+    workload: 36 copies of one 4B-class layer, so every launch reads fresh weights
+    from HBM.  One HIP graph per replay; GB/s per layer over algorithmic bytes."""
+    import torch
+    from w4a16_speculative_verify_amd.step import VerifyStep
+    st = VerifyStep(lins, None, None, 1, 1, 0)
+    x1 = x16[:1].contiguous()
+    st.linears_only(x1)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        st.linears_only(x1)
+    for _ in range(3):
+        g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / reps
+    layers = len(lins) // 4
+    b = sum(linear_bytes(1, l.k_in, l.n_out) for l in lins)
+    return {"layers": layers, "us_per_layer": round(us / layers, 2),
+            "bytes_per_layer": b // layers, "gbs": round(b / (us / 1e6) / 1e9, 1),
+            "pct_of_hbm_peak": round(100 * b / (us / 1e6) / 1e9 / HBM_PEAK_GBS, 2)}
+
+
+def padded_batch(lins, lm_w, lm_s, steps: int = 50, warmup: int = 5):
+    """Padded verify of 8 sequences x 21 rows (K = 20 drafts, -1 padding) through
+    one 4B-class layer and the 151,936-word int8 lm_head with fused argmax and
+    verify.  Weights: the first layer and the lm_head of the verify-step workload
+    (same shapes and distributions); activations and drafts: the padded
+    configuration's own seeded streams.  The linears at M = 168 run on the
+    LDS-tiled MFMA kernel."""
+    import numpy as np
+    import torch
+    import gen
+    from w4a16_speculative_verify_amd.step import VerifyStep
+    cfg = gen.CONFIGS[4]
+    dev = lm_w.device
+    r_x = gen.streams(1000 * cfg.cid, 4)[0]
+    x = torch.from_numpy(gen.activations(r_x, cfg.m, gen.HIDDEN)).to(dev)
+    st = VerifyStep(lins[:4], lm_w, lm_s, cfg.m, cfg.batch, cfg.k_draft)
+    none = torch.full((cfg.batch, cfg.k_draft), -1, dtype=torch.int32, device=dev)
+    t_ids, _, _, _ = st(x, none)
+    t_host = t_ids.cpu().numpy()
+    drng = gen.draft_rng(cfg.cid)
+    total = warmup + steps
+    d_all = np.empty((total, cfg.batch, cfg.k_draft), np.int32)
+    planned = np.empty((total, cfg.batch), np.int64)
+    for i in range(total):
+        d_all[i], planned[i] = gen.make_drafts(drng, cfg, t_host)
+    d_dev = torch.from_numpy(d_all).to(dev)
+    d_buf = torch.empty((cfg.batch, cfg.k_draft), dtype=torch.int32, device=dev)
+    acc = torch.zeros((total, cfg.batch), dtype=torch.int32, device=dev)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        st(x, d_buf)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g_step, g_lin = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g_step):
+        st(x, d_buf)
+    with torch.cuda.graph(g_lin):
+        st.linears_only(x)
+
+    def one(i):
+        d_buf.copy_(d_dev[i], non_blocking=True)
+        g_step.replay()
+        acc[i].copy_(st.accepted_len, non_blocking=True)
+
+    for i in range(warmup):
+        one(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(warmup, total):
+        one(i)
+    e1.record()
+    torch.cuda.synchronize()
+    step_us = e0.elapsed_time(e1) * 1e3 / steps
+    a = acc.cpu().numpy().astype(np.int64)
+    if not np.array_equal(a, planned):
+        raise RuntimeError("padded batch: accepted lengths differ from the planned ones")
+    for _ in range(3):
+        g_lin.replay()
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(steps):
+        g_lin.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    lin_us = e0.elapsed_time(e1) * 1e3 / steps
+    lin_flop = sum(2 * cfg.m * l.k_in * l.n_out for l in lins[:4])
+    head_flop = 2 * cfg.m * gen.HIDDEN * cfg.vocab
+    head_us = step_us - lin_us
+    head_b = lmhead_bytes(cfg.m, gen.HIDDEN, cfg.vocab, cfg.k_draft)
+    tokens = int(np.sum(a[warmup:] + 1))
+    return {"workload": "8 sequences x 21 rows (K=20, -1 padding): one 4B-class layer + int8 "
+                        "lm_head 2560->151936 + argmax + greedy verify", "m": cfg.m,
+            "step_us": round(step_us, 2), "linears_us": round(lin_us, 2),
+            "linears_tflops": round(lin_flop / (lin_us / 1e6) / 1e12, 1),
+            "linears_frac_of_fp16_mfma_peak": round(lin_flop / (lin_us / 1e6) / 1e12 / MFMA_FP16_PEAK_TFLOPS, 4),
+            "head_us": round(head_us, 2),
+            "head_tflops": round(head_flop / (head_us / 1e6) / 1e12, 1),
+            "head_gbs": round(head_b / (head_us / 1e6) / 1e9, 1),
+            "verified_tokens_per_s": round(tokens / (step_us * steps / 1e6), 1),
+            "mean_accepted_plus_one": round(tokens / (steps * cfg.batch), 3)}
+
+
 def drafter(dev, reps: int = 200):
     """Prompt-lookup drafting ahead of the verify (not part of the timed step):
     ngram_draft over B synthetic histories of 8192 tokens (half copied spans),
@@ -481,6 +595,11 @@ def main():
     gemm_gbs = lin_b / (lin_ms / 1e3) / 1e9
     step_gbs = (lin_b + lm_b) / (step_ms / 1e3) / 1e9
 
+    print("[bench] timing plain decode (M = 1) and the padded batch (M = 168)",
+          file=sys.stderr, flush=True)
+    m1 = decode_m1(lins, x)
+    padded = padded_batch(lins, step.lm_w, step.lm_s)
+
     pre = None
     if not args.no_prefill:
         print("[bench] timing the prefill-shaped linears", file=sys.stderr, flush=True)
@@ -547,6 +666,8 @@ def main():
                      "avg_launch_us": round(act_launch_us, 3)},
         "cpu_baseline": cpu,
         "prefill": pre,
+        "decode_m1": m1,
+        "padded_batch_m168": padded,
         "drafter": draft,
         "drafter_int4_step": dgemm,
         "g32_target_step": g32,
