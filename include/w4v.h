@@ -73,28 +73,31 @@ int w4v_abi_version(void);
  * Sizes    M >= 0 (M == 0 or N == 0: nothing to do, W4V_OK), K > 0,
  *          N % 8 == 0, K % group_size == 0; group_size must be 128 or 32,
  *          and K % 128 == 0 for both (W4V_ERR_UNSUPPORTED otherwise: the
- *          kernels step 128 k at a time).  For M < 512 the packed weights
- *          (K*N/2 bytes), the scales and the rows of x (M*ldx*2 bytes) must
- *          each stay below 2 GiB (W4V_ERR_UNSUPPORTED otherwise).
+ *          kernels step 128 k at a time).  On the in-register paths (M <= 32,
+ *          and M >= 33 without a workspace) the packed weights (K*N/2 bytes),
+ *          the scales and the rows of x (M*ldx*2 bytes) must each stay below
+ *          2 GiB (W4V_ERR_UNSUPPORTED otherwise).
  * alpha    epilogue scale applied to the fp32 accumulator before the single
  *          round-to-nearest-even to fp16.
  * Paths    M <= 32: weights dequantised exactly in registers, each group's
  *          scale applied to that group's fp32 sum (split-K across blocks).
- *          33 <= M < 512: the same arithmetic in an LDS-tiled MFMA kernel.
- *          M >= 512 (prefill shapes, bound by the matrix cores): the weights
+ *          M >= 33 (the batched verify block, prefill shapes: bound by the
+ *          matrix cores) with a workspace: the weights
  *          are first expanded to fp16 by this library's kernel,
  *          w = fp16_rne(float(s) * (q - z)) (one rounding; the fp32 product is
  *          exact), into the workspace, then multiplied by a plain fp16 GEMM of
  *          the vendor library (fp32 accumulation, same alpha and output
- *          rounding).  If the library offers no plan for the shape, the
- *          LDS-tiled kernel computes the product instead.
+ *          rounding).  M >= 33 with no workspace at all (NULL and 0 bytes),
+ *          or when the library offers no plan for the shape: the exact
+ *          in-register arithmetic of M <= 32 in an LDS-tiled MFMA kernel.
  * workspace  device memory of at least w4a16_gemm_workspace_size(M, N, K,
  *          group_size) bytes (may be NULL when that size is 0), 256-byte
  *          aligned, zeroed once by the caller.  Its first 64 KiB hold the
  *          split-K arrival counters (every call leaves them at zero), the next
- *          4 MiB at most the fp32 split-K partial sums (M <= 32); for M >= 512
+ *          4 MiB at most the fp32 split-K partial sums (M <= 32); for M >= 33
  *          the fp16 expanded weights (2*K*N bytes) and the library GEMM's
- *          scratch come after those 4 MiB.  The partials are added in split
+ *          scratch come after those 4 MiB.  M >= 33 with a workspace smaller
+ *          than the query's size (other than none at all): W4V_ERR_WORKSPACE.  The partials are added in split
  *          order, so the result does not depend on the order in which they
  *          arrive.  One workspace sized for the
  *          largest call serves calls of every shape ordered on one stream.

@@ -98,6 +98,16 @@ def test_gemm_workspace(lib):
     assert gemm(lib, K=4096, ldx=4096, g=32, ws=None, wsb=0) == WORKSPACE
     # sizes are a function of the shape alone
     assert w4v.gemm_workspace_size(16, 2560, 4096) == need
+    # from 33 rows on: the expanded fp16 weights and the library's scratch after the
+    # split-K regions; a partial workspace is an error, none at all selects the tiled kernel
+    big = w4v.gemm_workspace_size(33, 2560, 4096)
+    assert big >= 2 * 2560 * 4096 + (64 << 10) + (4 << 20)
+    assert w4v.gemm_workspace_size(168, 2560, 4096) == big == w4v.gemm_workspace_size(8192, 2560, 4096)
+    assert gemm(lib, M=33, K=4096, ldx=4096, ws=A * 256, wsb=big - 1) == WORKSPACE
+    assert gemm(lib, M=33, K=4096, ldx=4096, ws=A * 256, wsb=16) == WORKSPACE
+    # the tiled kernel keeps the 32-bit offset limits of the in-register paths
+    assert gemm(lib, M=64, N=65536, K=65536, ldx=65536, ldy=65536, y=1 << 40,
+                ws=None, wsb=0) == UNSUPPORTED
 
 
 def lm(lib, h=A, ldh=2560, w=A, sc=A, t=A, ml=None, M=16, H=2560, V=4096, ws=A * 256, wsb=1 << 30):

@@ -10,9 +10,9 @@ from tests.gpu_util import check_gemm, dev, host, log
 pytestmark = pytest.mark.gpu
 
 
-def run_gemm(w4v, x, lin, alpha=1.0, ws=None):
+def run_gemm(w4v, x, lin, alpha=1.0, ws=None, no_ws=False):
     y = w4v.w4a16_gemm(dev(x), dev(lin.qweight), dev(lin.scales), dev(lin.qzeros), alpha=alpha,
-                       workspace=ws)
+                       workspace=ws, no_workspace=no_ws)
     import torch
     torch.cuda.synchronize()
     return host(y)
@@ -29,8 +29,8 @@ def run_gemm(w4v, x, lin, alpha=1.0, ws=None):
     (16, 9728, 2560),          # deep K (split across blocks)
     (16, 4096, 2560),
     (3, 9728, 1032),
-    (33, 256, 200),            # tiled path: one ragged row past a 32-row block
-    (130, 384, 136),           # tiled path: ragged rows and columns
+    (33, 256, 200),            # expansion + library GEMM from one row past a 32-row block
+    (130, 384, 136),           # ragged rows and columns
     (300, 1280, 1032),
     (128, 128, 128),           # exactly one tile, one group
 ])
@@ -42,6 +42,43 @@ def test_random_shapes(lib, m, k, n):
     y = run_gemm(lib, x, lin)
     rel, mx = check_gemm(y, og.w4a16_gemm(x, lin.qweight, lin.scales, lin.qzeros), f"{m}x{k}x{n}")
     log(f"  rel-L2 {rel:.2e} max/rms {mx:.2e}")
+
+
+# ---- M >= 33 without a workspace: the LDS-tiled kernel (exact in-register dequantisation)
+@pytest.mark.parametrize("m,k,n", [
+    (33, 256, 200),            # one ragged row past a 32-row block
+    (130, 384, 136),           # ragged rows and columns
+    (300, 1280, 1032),
+    (128, 128, 128),           # exactly one tile, one group
+    (168, 2560, 2560),         # the padded verify batch of 8 x 21 rows
+    (600, 1280, 520),          # prefill-sized M on the tiled kernel
+])
+def test_tiled_kernel_without_workspace(lib, m, k, n):
+    log(f"gemm tiled m={m} k={k} n={n}")
+    rng = np.random.default_rng(7000 + m * 7 + k + n)
+    lin = gen.qlinear(rng, k, n)
+    x = gen.activations(rng, m, k)
+    y = run_gemm(lib, x, lin, alpha=0.75, no_ws=True)
+    rel, mx = check_gemm(y, og.w4a16_gemm(x, lin.qweight, lin.scales, lin.qzeros, alpha=0.75),
+                         f"tiled {m}x{k}x{n}")
+    log(f"  rel-L2 {rel:.2e} max/rms {mx:.2e}")
+
+
+@pytest.mark.parametrize("enc", range(3))
+@pytest.mark.parametrize("m", [64, 200])
+def test_tiled_kernel_identity_bit_exact(lib, enc, m):
+    n = 512
+    eye = np.eye(n, dtype=np.int64)
+    g = n // 128
+    q, z, s = [
+        (eye, np.zeros((g, n), np.int64), np.ones((g, n), np.float16)),
+        (8 + eye, np.full((g, n), 8, np.int64), np.ones((g, n), np.float16)),
+        (7 + 2 * eye, np.full((g, n), 7, np.int64), np.full((g, n), 0.5, np.float16)),
+    ][enc]
+    lin = gen.QLinear(gen.pack_int4_along_k(q), s, gen.pack_int4_along_n(z), n, n)
+    x = gen.activations(np.random.default_rng(enc + 40), m, n)
+    y = run_gemm(lib, x, lin, no_ws=True)
+    assert np.array_equal(y.view(np.uint16), x.view(np.uint16))
 
 
 @pytest.mark.parametrize("enc", range(3))
@@ -167,10 +204,11 @@ def test_large_m_sampled_columns(lib, m, shape):
     assert np.all(np.isfinite(y.astype(np.float32)))
 
 
-# ---- M >= 512: weights dequantised to fp16 by the library's kernel, then a plain fp16 GEMM
+# ---- M >= 33 with a workspace: weights dequantised to fp16 by the library's kernel, then a
+# plain fp16 GEMM
 @pytest.mark.parametrize("m,k,n", [
-    (511, 384, 136),           # last row count of the tiled kernel
-    (512, 384, 136),           # first row count of the dequantise + GEMM path, ragged N
+    (511, 384, 136),
+    (512, 384, 136),           # ragged N
     (600, 1280, 1032),
     (1000, 128, 8),            # one group, narrowest N
 ])

@@ -1,6 +1,6 @@
 """GPU parity of the W4A16 linear at group size 32 (results page, section 5:
 team #5's compressed-tensors target) against the fp64 oracle on all three
-paths (M <= 32 skinny, 33..511 LDS-tiled, >= 512 expansion + library GEMM),
+paths (M <= 32 skinny; M >= 33 expansion + library GEMM, or LDS-tiled without a workspace),
 exact identity and one-hot cases whose scale and zero-point change every 32 k,
 and the 4B-class layer's linears at M = 16."""
 import numpy as np
@@ -14,10 +14,10 @@ pytestmark = pytest.mark.gpu
 GS = 32
 
 
-def run_gemm(w4v, x, lin, alpha=1.0, ws=None):
+def run_gemm(w4v, x, lin, alpha=1.0, ws=None, no_ws=False):
     import torch
     y = w4v.w4a16_gemm(dev(x), dev(lin.qweight), dev(lin.scales), dev(lin.qzeros), alpha=alpha,
-                       workspace=ws, group_size=GS)
+                       workspace=ws, group_size=GS, no_workspace=no_ws)
     torch.cuda.synchronize()
     return host(y)
 
@@ -28,26 +28,31 @@ def run_gemm(w4v, x, lin, alpha=1.0, ws=None):
     (21, 1280, 520),           # K = 20 verify block: two m-tiles
     (16, 9728, 2560),          # deep K: split across blocks
     (5, 128, 8),               # one 128-k step, four groups, narrowest N
-    (33, 256, 200),            # tiled path, ragged rows and columns
+    (33, 256, 200),            # expansion + library GEMM, ragged rows and columns
     (200, 1280, 1032),
-    (512, 384, 136),           # expansion + library GEMM
+    (512, 384, 136),
     (640, 1280, 1032),
 ])
-def test_random_shapes_group_32(lib, m, k, n):
-    log(f"gemm g32 m={m} k={k} n={n}")
+@pytest.mark.parametrize("no_ws", [False, True])
+def test_random_shapes_group_32(lib, m, k, n, no_ws):
+    if no_ws and m <= 32:
+        pytest.skip("the in-register split-K path needs its workspace")
+    log(f"gemm g32 m={m} k={k} n={n} no_ws={no_ws}")
     rng = np.random.default_rng(5000 + m + k + n)
     lin = gen.qlinear(rng, k, n, group_size=GS)
     x = gen.activations(rng, m, k)
-    y = run_gemm(lib, x, lin, alpha=0.75)
+    y = run_gemm(lib, x, lin, alpha=0.75, no_ws=no_ws)
     rel, mx = check_gemm(y, og.w4a16_gemm(x, lin.qweight, lin.scales, lin.qzeros, alpha=0.75,
                                           group_size=GS), f"g32 {m}x{k}x{n}")
     log(f"  rel-L2 {rel:.2e} max/rms {mx:.2e}")
 
 
 @pytest.mark.parametrize("enc", range(3))
-@pytest.mark.parametrize("m", [16, 21, 64, 640])
-def test_identity_weights_bit_exact_group_32(lib, enc, m):
-    """q - z in {0, 1} (or {0, 2} at scale 0.5) with the zero-point changing every 32 k."""
+@pytest.mark.parametrize("m,no_ws", [(16, False), (21, False), (64, False), (640, False),
+                                     (64, True), (200, True)])
+def test_identity_weights_bit_exact_group_32(lib, enc, m, no_ws):
+    """q - z in {0, 1} (or {0, 2} at scale 0.5) with the zero-point changing every 32 k
+    (no_ws: the LDS-tiled kernel)."""
     n = 512
     g = n // GS
     eye = np.eye(n, dtype=np.int64)
@@ -60,12 +65,12 @@ def test_identity_weights_bit_exact_group_32(lib, enc, m):
     ][enc]
     lin = gen.QLinear(gen.pack_int4_along_k(q), s, gen.pack_int4_along_n(z), n, n, GS)
     x = gen.activations(np.random.default_rng(enc + m), m, n)
-    y = run_gemm(lib, x, lin)
+    y = run_gemm(lib, x, lin, no_ws=no_ws)
     assert np.array_equal(y.view(np.uint16), x.view(np.uint16))
 
 
-@pytest.mark.parametrize("m", [16, 64])
-def test_one_hot_weight_with_per_group_scales(lib, m):
+@pytest.mark.parametrize("m,no_ws", [(16, False), (64, False), (64, True)])
+def test_one_hot_weight_with_per_group_scales(lib, m, no_ws):
     """A single nonzero weight in the third 32-k group of a 128-k step; every group has
     its own scale and zero-point, so a group index off by one changes the result."""
     k, n = 512, 264
@@ -78,7 +83,7 @@ def test_one_hot_weight_with_per_group_scales(lib, m):
     z = np.repeat(zg[:, None], n, 1)
     lin = gen.QLinear(gen.pack_int4_along_k(q), s.astype(np.float16), gen.pack_int4_along_n(z), k, n, GS)
     x = gen.activations(np.random.default_rng(9 + m), m, k)
-    y = run_gemm(lib, x, lin)
+    y = run_gemm(lib, x, lin, no_ws=no_ws)
     w = float(s[k0 // GS, n0]) * float(q[k0, n0] - zg[k0 // GS])
     expect = np.zeros((m, n), dtype=np.float16)
     expect[:, n0] = (x[:, k0].astype(np.float64) * w).astype(np.float16)

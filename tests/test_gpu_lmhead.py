@@ -27,7 +27,8 @@ def run_lm(w4v, h, w8, s8, ws=None):
 
 
 @pytest.mark.parametrize("m,v", [(16, 4096), (1, 4096), (21, 1000), (16, 4097), (40, 777),
-                                 (168, 5000), (16, 70000), (3, 1)])
+                                 (168, 5000), (16, 70000), (3, 1),
+                                 (64, 3000), (65, 4099), (97, 2000), (200, 777)])
 def test_random(lib, m, v):
     log(f"lmhead m={m} v={v}")
     rng = np.random.default_rng(m * 31 + v)
@@ -42,9 +43,10 @@ def test_random(lib, m, v):
     log(f"  low-margin rows {low}/{m}")
 
 
-def test_ties_go_to_lowest_index(lib):
-    rng = np.random.default_rng(5)
-    v, m = 20000, 16
+@pytest.mark.parametrize("m", [16, 100])
+def test_ties_go_to_lowest_index(lib, m):
+    rng = np.random.default_rng(5 + m)
+    v = 25000
     w8 = gen.lmhead_weights(rng, v, gen.HIDDEN)
     s8 = np.full(v, 0.002, dtype=np.float16)
     h = gen.activations(rng, m, gen.HIDDEN)

@@ -151,13 +151,14 @@ def new_workspace(nbytes: int, device="cuda"):
 
 # ------------------------------------------------------------------- calls
 def w4a16_gemm(x, qweight, scales, qzeros, alpha: float = 1.0, out=None, workspace=None,
-               group_size: int = GROUP_SIZE, stream=None):
+               group_size: int = GROUP_SIZE, stream=None, no_workspace: bool = False):
     """y[M, N] = fp16(alpha * x[:, :K] @ dequant(qweight, scales, qzeros)).
 
     x: fp16 [M, >=K] (a column slice of a wider tensor is fine: its row stride
     is passed as ldx); qweight: int32 [K/8, N]; scales: fp16 [K/g, N];
     qzeros: int32 [K/g, N/8] with g = group_size (128 or 32).  ``out`` may be a
-    row-strided fp16 [M, N] view.
+    row-strided fp16 [M, N] view.  ``no_workspace`` passes none at all (for
+    M >= 33 the library then runs its LDS-tiled kernel).
     """
     torch = _require(x, __import__("torch").float16, "x")
     _require(qweight, torch.int32, "qweight")
@@ -176,7 +177,9 @@ def w4a16_gemm(x, qweight, scales, qzeros, alpha: float = 1.0, out=None, workspa
         out = torch.empty((m, n), dtype=torch.float16, device=x.device)
     _require(out, torch.float16, "out")
     need = gemm_workspace_size(m, n, k, group_size)
-    if workspace is None and need > 0:
+    if no_workspace:
+        workspace = None
+    elif workspace is None and need > 0:
         workspace = new_workspace(need, x.device)
     wbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     st = load().w4a16_gemm(_ptr(x), x.stride(0), _ptr(qweight), _ptr(scales), _ptr(qzeros),

@@ -73,7 +73,7 @@ int run_lmhead(const void* h, int64_t ldh, const void* w, const void* scales, in
                const int32_t* draft_ids, int B, int K, int32_t* accepted_len,
                int32_t* out_tokens, void* workspace, size_t workspace_bytes, void* stream) {
   const w4v::LmheadPlan p = w4v::plan_lmhead(M, H, V, kPlanCUs);
-  if (p.mblocks > kMaxGridYZ) return W4V_ERR_UNSUPPORTED;
+  if (p.vblocks > kMaxGridYZ) return W4V_ERR_UNSUPPORTED;    // grid y
   int st = workspace_check(p.workspace_bytes(), workspace, workspace_bytes);
   if (st != W4V_OK) return st;
   w4v::LmheadArgs a{};
@@ -246,7 +246,6 @@ size_t w4a16_gemm_workspace_size(int M, int N, int K, int group_size) {
       K % w4v::kGroup != 0 || N % 8 != 0)
     return 0;
   if (M >= w4v::kLibMinRows) return lib_workspace_bytes(N, K);
-  if (M >= w4v::kTiledMinRows) return 0;
   return w4v::plan_w4a16(M, N, K, kPlanCUs).workspace_bytes();
 }
 
@@ -255,8 +254,11 @@ int w4a16_gemm(const void* x, int64_t ldx, const int32_t* qweight, const void* s
                float alpha, void* workspace, size_t workspace_bytes, void* stream) {
   int st = gemm_check(x, ldx, qweight, scales, qzeros, y, ldy, M, N, K, group_size);
   if (st != W4V_OK || M == 0 || N == 0) return st;
-  const bool lib = M >= w4v::kLibMinRows;
-  const bool tiled = M >= w4v::kTiledMinRows;
+  // 33 rows and more: the library path with a workspace, the LDS-tiled
+  // kernel (no workspace needed) when none is given at all
+  const bool many = M >= w4v::kTiledMinRows;
+  const bool lib = many && M >= w4v::kLibMinRows && !(workspace == nullptr && workspace_bytes == 0);
+  const bool tiled = many;
   if (tiled && (M + 127) / 128 > kMaxGridYZ) return W4V_ERR_UNSUPPORTED;
   // buffer resources take 32-bit offsets below 2 GiB
   const bool big = (size_t)K * N / 2 >= (1ull << 31) || (size_t)M * ldx * 2 >= (1ull << 31) ||

@@ -59,9 +59,10 @@ hipError_t launch_w4a16_skinny(const GemmArgs& a, const GemmPlan& p, void* works
 hipError_t launch_w4a16_tiled(const GemmArgs& a, hipStream_t stream);
 constexpr int kTiledMinRows = 33;
 
-// From this many rows on: weights dequantised to a transposed fp16 copy in the
-// workspace, then a plain fp16 GEMM from the vendor library.
-constexpr int kLibMinRows = 512;
+// From this many rows on, with a workspace: weights dequantised to a
+// transposed fp16 copy in the workspace, then a plain fp16 GEMM from the
+// vendor library (without a workspace: the LDS-tiled kernel).
+constexpr int kLibMinRows = 33;
 constexpr size_t kLibWorkspace = 64ull << 20;   // the library GEMM's own scratch
 hipError_t launch_dequant_w4_f16t(const uint32_t* qweight, const _Float16* scales,
                                   const uint32_t* qzeros, int K, int N, int group_size,
@@ -87,7 +88,7 @@ struct LmheadArgs {
 };
 
 struct LmheadPlan {
-  int mt;            // 16-row m-tiles per block (1 or 2)
+  int mt;            // 16-row m-tiles per block (1, 2, 4 or 6)
   int mblocks;
   int tiles;         // 16-row vocabulary tiles per wave pass (1 or 2)
   int depth;         // steps in flight per wave (3)
