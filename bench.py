@@ -474,6 +474,8 @@ def main():
                          "4-bit drafter step, recurrent-state commit)")
     ap.add_argument("--no-g32", action="store_true",
                     help="skip the group-size-32 target step (fp16 first and last layers)")
+    ap.add_argument("--no-other-m", action="store_true",
+                    help="skip the plain-decode (M = 1) and padded-batch (M = 168) timings")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="one device-to-device copy of this many MiB before timing (counter calibration)")
@@ -595,10 +597,12 @@ def main():
     gemm_gbs = lin_b / (lin_ms / 1e3) / 1e9
     step_gbs = (lin_b + lm_b) / (step_ms / 1e3) / 1e9
 
-    print("[bench] timing plain decode (M = 1) and the padded batch (M = 168)",
-          file=sys.stderr, flush=True)
-    m1 = decode_m1(lins, x)
-    padded = padded_batch(lins, step.lm_w, step.lm_s)
+    m1 = padded = None
+    if not args.no_other_m:
+        print("[bench] timing plain decode (M = 1) and the padded batch (M = 168)",
+              file=sys.stderr, flush=True)
+        m1 = decode_m1(lins, x)
+        padded = padded_batch(lins, step.lm_w, step.lm_s)
 
     pre = None
     if not args.no_prefill:
