@@ -389,40 +389,50 @@ GemmPlan plan_w4a16(int M, int N, int K, int num_cus) {
   p.mblocks = (M + rows_blk - 1) / rows_blk;
   p.tiles = (N + kColTile - 1) / kColTile;
   const int G = K / kGroup;
-  // Four k-slices per block (added through LDS); one 64-column tile per block,
-  // two when the tiles alone outnumber the CUs.  The split-K factor minimises
-  // the steps of the longest wave times the rounds of waves per SIMD, the
-  // fewest splits on ties, with at most two blocks per CU once the groups are
-  // split.  On MI355X this picks the best or near-best of the measured
-  // tile / k-slice / split / depth choices for the 4B-class verify shapes at
-  // M = 16 (QKV 5 splits, O 4, down 5, gate+up 1 with two tiles per block).
+  // Four k-slices per block (added through LDS); one or two 64-column tiles
+  // per block, and a split-K factor, chosen to minimise the steps of the
+  // longest wave times its rounds (blocks per CU, times waves per SIMD within a
+  // block), one tile and the fewest splits on ties.  Measured on MI355X for the
+  // 4B-class verify shapes:
+  //   - 16-row blocks: one tile, at most two blocks per CU once split (QKV 5
+  //     splits, O 4, down 5);
+  //   - 32-row blocks (the group-32 target at M = 24): at most one block per
+  //     CU, and two tiles may share a block, so that a tile pair shares its
+  //     twice-as-large activation tile (QKV 12.7 -> 10.3 us with two tiles x
+  //     5 splits);
+  //   - tiles outnumbering the CUs (gate+up, 304 tiles): two tiles per block
+  //     and no split (15.2 us at 3 splits against 10.8 us unsplit).
   p.wk = 4;
-  p.wt = ((long)p.tiles * p.mblocks > num_cus) ? 2 : 1;
-  p.col_blocks = (p.tiles + p.wt - 1) / p.wt;
-  const long simds = 4L * num_cus;
-  const size_t part_per_split = (size_t)p.mblocks * rows_blk * p.col_blocks * p.wt * kColTile *
-                                sizeof(float);
-  // no split once two tiles share a block: gate+up (304 tiles) measured 15.2 us
-  // at 3 splits against 10.8 us unsplit, although the step count favours the split
-  const int smax = (p.wt == 1 && (size_t)p.tiles * p.mblocks <= kMaxTickets) ? G : 1;
+  const bool wide = (long)p.tiles * p.mblocks > num_cus;
+  const long max_blocks = (p.mt == 1 ? 2L : 1L) * num_cus;
+  const int smax = (!wide && (size_t)p.tiles * p.mblocks <= kMaxTickets) ? G : 1;
   int splits = 1;
   long best = -1;
-  for (int s = 1; s <= smax; ++s) {
-    const long blocks = (long)p.col_blocks * p.mblocks * s;
-    if (s > 1 && (blocks > 2L * num_cus || part_per_split * s > kPartialRegion)) break;
-    const long steps = ((G + s - 1) / s + p.wk - 1) / p.wk;   // of the longest wave
-    const long waves = blocks * p.wt * p.wk;
-    const long cost = steps * ((waves + simds - 1) / simds);
-    if (best < 0 || cost < best) {
-      best = cost;
-      splits = s;
+  for (int wt = 1; wt <= 2; ++wt) {
+    if ((wt == 1 && wide) || (wt == 2 && !wide && p.mt == 1)) continue;
+    const int cb = (p.tiles + wt - 1) / wt;
+    const size_t part_per_split =
+        (size_t)p.mblocks * rows_blk * cb * wt * kColTile * sizeof(float);
+    for (int s = 1; s <= smax; ++s) {
+      const long blocks = (long)cb * p.mblocks * s;
+      if (s > 1 && (blocks > max_blocks || part_per_split * s > kPartialRegion)) break;
+      const long steps = ((G + s - 1) / s + p.wk - 1) / p.wk;   // of the longest wave
+      const long rounds = ((blocks + num_cus - 1) / num_cus) * ((wt * p.wk + 3) / 4);
+      const long cost = steps * rounds;
+      if (best < 0 || cost < best) {
+        best = cost;
+        splits = s;
+        p.wt = wt;
+      }
     }
   }
+  p.col_blocks = (p.tiles + p.wt - 1) / p.wt;
   p.splits = splits;
   p.depth = 3;
   if (splits > 1) {
     p.ticket_bytes = kTicketRegion;
-    p.partial_bytes = part_per_split * splits;
+    p.partial_bytes = (size_t)p.mblocks * rows_blk * p.col_blocks * p.wt * kColTile *
+                      sizeof(float) * splits;
   }
   return p;
 }
