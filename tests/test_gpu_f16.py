@@ -15,7 +15,10 @@ pytestmark = pytest.mark.gpu
 
 @pytest.mark.parametrize("m,k,n", [
     (16, 2560, 6144), (16, 4096, 2560), (16, 2560, 19456), (16, 9728, 2560),
-    (1, 2560, 520), (5, 384, 136), (21, 1280, 1032), (640, 1280, 1032),
+    (24, 2560, 6144), (24, 9728, 2560),          # the verify block of K = 23
+    (1, 2560, 520), (5, 384, 136), (21, 1280, 1032), (32, 128, 8),
+    (16, 200, 136), (24, 1000, 520),             # K not a multiple of 128
+    (33, 1280, 1032), (640, 1280, 1032),
 ])
 def test_f16_linear_shapes(lib, m, k, n):
     import torch
