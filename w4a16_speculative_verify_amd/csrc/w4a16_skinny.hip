@@ -100,6 +100,7 @@ __device__ __forceinline__ void store_row4(_Float16* dst, float a0, float a1, fl
 // trip to memory per batch; loads past the last split are masked off)
 template <int MT, int WT, int WK, int D, int SB, int Q>
 __global__ __launch_bounds__(64 * WT * WK) void w4a16_skinny_kernel(GemmArgs a, int splits,
+                                                                    int gbase, int grem,
                                                                     unsigned* tickets,
                                                                     float* partials) {
   constexpr int NW = WT * WK;                       // waves per block
@@ -116,10 +117,12 @@ __global__ __launch_bounds__(64 * WT * WK) void w4a16_skinny_kernel(GemmArgs a, 
   const int kb = lane >> 4, chunk = lane & 15;
   const int mbase = mblk * 16 * MT;
 
-  // groups of this split, then of this k-slice (G * splits < 2^31: 32-bit division)
-  const int gs0 = (int)((unsigned)(G * split) / (unsigned)splits);
-  const int gs1 = (int)((unsigned)(G * (split + 1)) / (unsigned)splits);
-  const int glen = gs1 - gs0;
+  // groups of this split, then of this k-slice: the first grem splits take
+  // gbase + 1 groups, the others gbase (G / splits and G % splits, from the
+  // host: a division here would put some fifty dependent instructions in
+  // front of the first load)
+  const int gs0 = split * gbase + (split < grem ? split : grem);
+  const int glen = gbase + (split < grem ? 1 : 0);
   const int g0 = gs0 + glen * wk / WK;
   const int n = gs0 + glen * (wk + 1) / WK - g0;   // groups of this wave
   const int nmax = (glen + WK - 1) / WK;            // steps of the block
@@ -359,9 +362,10 @@ __global__ __launch_bounds__(64 * WT * WK) void w4a16_skinny_kernel(GemmArgs a, 
 template <int MT, int WT, int WK, int D, int SB, int Q>
 void launch_t(const GemmArgs& a, const GemmPlan& p, unsigned* tickets, float* partials,
               hipStream_t stream) {
+  const int G = a.K / kGroup;
   hipLaunchKernelGGL((w4a16_skinny_kernel<MT, WT, WK, D, SB, Q>),
                      dim3(p.col_blocks, p.splits, p.mblocks), dim3(64 * WT * WK), 0, stream, a,
-                     p.splits, tickets, partials);
+                     p.splits, G / p.splits, G % p.splits, tickets, partials);
 }
 
 // Four k-slices per block, one or two tiles, three steps in flight per wave;
