@@ -116,7 +116,7 @@ def counter_traffic():
 
 def prefill(dev, reps: int = 10):
     """The prefill-shaped linears (gate+up 2560->19456, down 9728->2560) at
-    M = 2048 and 8192 through w4a16_gemm (at M >= 512: the weights expanded to
+    M = 2048 and 8192 through w4a16_gemm (from 33 rows on: the weights expanded to
     fp16 by the library's kernel, then a plain fp16 GEMM): TFLOP/s per shape,
     2*M*K*N flops over the average of ``reps`` back-to-back calls, each call
     including its weight expansion."""

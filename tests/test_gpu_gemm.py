@@ -242,7 +242,7 @@ def test_library_path_identity_bit_exact(lib, enc):
 
 def test_library_path_strided_and_shared_workspace(lib):
     """Row-strided x and y at M = 700, then M = 16 split-K calls on the same workspace: the
-    counter prefix the split-K path relies on is left at zero by the M >= 512 path."""
+    counter prefix the split-K path relies on is left at zero by the expanded-weight path."""
     import torch
     rng = np.random.default_rng(31)
     k, n, m = 1024, 520, 700

@@ -1,8 +1,10 @@
-// W4A16 weights expanded to fp16 for the prefill-shaped linear, gfx950.
-// Section 4 of the organisers' results page puts long prompts in prefill
-// compute: at M >= 512 rows the product is a dense contraction bound by the
-// matrix cores, and a plain fp16 GEMM on dequantised weights runs it at
-// about twice the rate of the fused in-register kernel (measured on MI355X).
+// W4A16 weights expanded to fp16 for the linear at 33 rows and more (the
+// batched verify block, prefill shapes), gfx950.  Section 4 of the
+// organisers' results page puts long prompts in prefill compute: there the
+// product is a dense contraction bound by the matrix cores, and a plain fp16
+// GEMM on dequantised weights runs it at about twice the rate of the fused
+// in-register kernel; at the batched verify block (M = 168) the pair is also
+// twice as fast as that kernel, which has too few blocks (measured on MI355X).
 //
 //   wt[n, k] = fp16_rne( float(s[k/gs, n]) * (q[k, n] - z[k/gs, n]) ),  gs = 128 or 32
 //

@@ -1,5 +1,8 @@
-// W4A16 linear for many activation rows (prefill-shaped, and the batched
-// verify block of several sequences), gfx950: an LDS-tiled MFMA GEMM.
+// W4A16 linear for many activation rows without a workspace (prefill-shaped,
+// the batched verify block of several sequences; with a workspace the
+// library expands the weights to fp16 and runs a plain GEMM instead, and
+// this kernel is its fallback when no plan exists), gfx950: an LDS-tiled
+// MFMA GEMM with the exact in-register dequantisation.
 // Section 4 of the organisers' results page puts the long-prompt cost in
 // prefill compute; at M = 2,048-8,192 rows the W4A16 linear is a dense
 // contraction bound by the matrix cores, not by HBM.

@@ -20,8 +20,8 @@ constexpr int kWorkspaceAlign = 256;
 // one stream.
 constexpr size_t kTicketRegion = 64 * 1024;
 // Split-K partials of the skinny linear follow the counter prefix and never
-// exceed this many bytes (the plan keeps splits x blocks <= 192 blocks of at
-// most 32 rows x 128 columns of fp32); other paths place their data after it.
+// exceed this many bytes (the plan keeps them within it); other paths place
+// their data after it.
 constexpr size_t kPartialRegion = 4u << 20;
 constexpr size_t kTicketStride = 64;            // 32-bit words between two counters
 constexpr size_t kMaxTickets = kTicketRegion / (kTicketStride * sizeof(unsigned));
