@@ -60,7 +60,8 @@ def test_f16_linear_strided_and_graph_replay(lib):
         assert np.array_equal(host(y).view(np.uint16), eager.view(np.uint16)), rep
 
 
-@pytest.mark.parametrize("m,v", [(16, 4096), (16, 151936), (21, 50000), (1, 300)])
+@pytest.mark.parametrize("m,v", [(16, 4096), (16, 151936), (21, 50000), (1, 300),
+                                 (64, 3000), (100, 4099), (168, 20000)])   # 64- and 96-row blocks
 def test_f16_lmhead_argmax(lib, m, v):
     import torch
     rng = np.random.default_rng(8000 + m + v)
