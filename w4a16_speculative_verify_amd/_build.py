@@ -37,10 +37,15 @@ def _hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build libw4v)")
 
 
+# per-source flags: the skinny W4A16 kernel takes its first 14 argument dwords
+# preloaded into SGPRs (the scalars its first group step needs)
+SOURCE_FLAGS = {"w4a16_skinny.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=14"]}
+
+
 def _compile(src: str, hipcc: str, verbose: bool) -> str:
     obj = os.path.join(OBJDIR, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc, *HIP_FLAGS, "-x", "hip", "-I", INCLUDE, "-I", CSRC, "-c",
-           os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc, *HIP_FLAGS, *SOURCE_FLAGS.get(src, []), "-x", "hip", "-I", INCLUDE, "-I", CSRC,
+           "-c", os.path.join(CSRC, src), "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if verbose or res.returncode != 0:
         msg = "\n".join(l for l in (res.stdout + res.stderr).splitlines()

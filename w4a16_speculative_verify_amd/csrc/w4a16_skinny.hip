@@ -98,11 +98,16 @@ __device__ __forceinline__ void store_row4(_Float16* dst, float a0, float a1, fl
 
 // SB: split-K partials the last block of a tile loads per batch (one round
 // trip to memory per batch; loads past the last split are masked off)
+// Everything the first group step needs comes first, as scalars (pointers to
+// the weights, scales, zero-points and activations, N, M, the activation row
+// stride, the split parameters): the library builds this kernel with those 14
+// dwords preloaded into SGPRs, so the prologue's loads issue without waiting
+// for argument loads; the rest of GemmArgs is needed only by the epilogue.
 template <int MT, int WT, int WK, int D, int SB, int Q>
-__global__ __launch_bounds__(64 * WT * WK) void w4a16_skinny_kernel(GemmArgs a, int splits,
-                                                                    int gbase, int grem,
-                                                                    unsigned* tickets,
-                                                                    float* partials) {
+__global__ __launch_bounds__(64 * WT * WK) void w4a16_skinny_kernel(
+    const uint32_t* pqw, const _Float16* psc, const uint32_t* pqz, const _Float16* px, int pN,
+    int pM, int pldx, int splits, int gbase, int grem, GemmArgs a, unsigned* tickets,
+    float* partials) {
   constexpr int NW = WT * WK;                       // waves per block
   constexpr int kXWords = MT * 16 * kXRowWords;     // one group's activation tile
   const int lane = threadIdx.x & 63;
@@ -111,8 +116,7 @@ __global__ __launch_bounds__(64 * WT * WK) void w4a16_skinny_kernel(GemmArgs a, 
   const int cb = blockIdx.x;
   const int split = blockIdx.y;
   const int mblk = blockIdx.z;
-  const int G = a.K / kGroup;
-  const int T = (a.N + kColTile - 1) / kColTile;
+  const int T = (pN + kColTile - 1) / kColTile;
   const int tile = cb * WT + wt;
   const int kb = lane >> 4, chunk = lane & 15;
   const int mbase = mblk * 16 * MT;
@@ -128,8 +132,8 @@ __global__ __launch_bounds__(64 * WT * WK) void w4a16_skinny_kernel(GemmArgs a, 
   const int nmax = (glen + WK - 1) / WK;            // steps of the block
 
   const int col_raw = tile * kColTile + 4 * chunk;
-  const bool colok = tile < T && col_raw < a.N;     // N % 8 == 0: 4 columns all valid or none
-  const int col = colok ? col_raw : a.N - 4;        // the column this lane reads
+  const bool colok = tile < T && col_raw < pN;      // N % 8 == 0: 4 columns all valid or none
+  const int col = colok ? col_raw : pN - 4;         // the column this lane reads
 
   constexpr int E = MT * 16;                        // accumulator floats per lane
   constexpr int kTileWords = 2 * WK * kXWords;      // double-buffered activation tiles
@@ -144,11 +148,11 @@ __global__ __launch_bounds__(64 * WT * WK) void w4a16_skinny_kernel(GemmArgs a, 
     for (int c = 0; c < 4; ++c) acc[mt][c] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   Resources rs;
-  rs.w = make_rsrc(a.qweight);
-  rs.z = make_rsrc(a.qzeros);
-  rs.s = make_rsrc(a.scales);
-  rs.x = make_rsrc(a.x);
-  const uint32_t N = (uint32_t)a.N;
+  rs.w = make_rsrc(pqw);
+  rs.z = make_rsrc(pqz);
+  rs.s = make_rsrc(psc);
+  rs.x = make_rsrc(px);
+  const uint32_t N = (uint32_t)pN;
   Lanes<MT, WT> o;
   o.w = ((uint32_t)kb * N + col) * 4;
   o.wq = 16 * N;                                    // 4 packed rows
@@ -160,8 +164,8 @@ __global__ __launch_bounds__(64 * WT * WK) void w4a16_skinny_kernel(GemmArgs a, 
 #pragma unroll
   for (int q = 0; q < Frag<MT, WT, Q>::kXLoads; ++q) {
     int m = mbase + xrow_of(q * WT + wt, lane);
-    m = m < a.M ? m : a.M - 1;                      // rows past M: never stored
-    o.x[q] = ((uint32_t)m * (uint32_t)a.ldx + chunk * 8) * 2;
+    m = m < pM ? m : pM - 1;                        // rows past M: never stored
+    o.x[q] = ((uint32_t)m * (uint32_t)pldx + chunk * 8) * 2;
   }
   const uint32_t magic = in_vgpr(0x64006400u);
   const int zshift = (lane & 1) * 16;
@@ -364,8 +368,9 @@ void launch_t(const GemmArgs& a, const GemmPlan& p, unsigned* tickets, float* pa
               hipStream_t stream) {
   const int G = a.K / kGroup;
   hipLaunchKernelGGL((w4a16_skinny_kernel<MT, WT, WK, D, SB, Q>),
-                     dim3(p.col_blocks, p.splits, p.mblocks), dim3(64 * WT * WK), 0, stream, a,
-                     p.splits, G / p.splits, G % p.splits, tickets, partials);
+                     dim3(p.col_blocks, p.splits, p.mblocks), dim3(64 * WT * WK), 0, stream,
+                     a.qweight, a.scales, a.qzeros, a.x, a.N, a.M, (int)a.ldx, p.splits,
+                     G / p.splits, G % p.splits, a, tickets, partials);
 }
 
 // Four k-slices per block, one or two tiles, three steps in flight per wave;
