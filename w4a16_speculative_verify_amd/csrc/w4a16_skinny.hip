@@ -73,12 +73,19 @@ struct Lanes {
 __device__ __forceinline__ int xrow_of(int i, int lane) { return 4 * i + (lane >> 4); }
 
 template <int MT, int WT, int Q>
-__device__ __forceinline__ void load_group(Frag<MT, WT, Q>& f, const Resources& rs,
-                                           const Lanes<MT, WT>& o, int g, bool valid) {
+__device__ __forceinline__ void load_weights(Frag<MT, WT, Q>& f, const Resources& rs,
+                                             const Lanes<MT, WT>& o, int g, bool valid) {
   const uint32_t gg = (uint32_t)g;
 #pragma unroll
   for (int it = 0; it < 4; ++it)
     f.w[it] = ld_x4<kNT>(rs.w, o.w + it * o.wq + (valid ? gg * o.gw : kNoLoad));
+}
+
+// the rest of a group: zero-points, scales, activations (issued after its weights)
+template <int MT, int WT, int Q>
+__device__ __forceinline__ void load_rest(Frag<MT, WT, Q>& f, const Resources& rs,
+                                          const Lanes<MT, WT>& o, int g, bool valid) {
+  const uint32_t gg = (uint32_t)g;
 #pragma unroll
   for (int q = 0; q < Q; ++q) {
     f.zw[q] = ld_x1(rs.z, o.z + (valid ? (gg * Q + q) * o.gz : kNoLoad));
@@ -87,6 +94,13 @@ __device__ __forceinline__ void load_group(Frag<MT, WT, Q>& f, const Resources& 
 #pragma unroll
   for (int q = 0; q < Frag<MT, WT, Q>::kXLoads; ++q)
     f.x[q] = ld_x4(rs.x, o.x[q] + (valid ? gg * (uint32_t)(kGroup * 2) : kNoLoad));
+}
+
+template <int MT, int WT, int Q>
+__device__ __forceinline__ void load_group(Frag<MT, WT, Q>& f, const Resources& rs,
+                                           const Lanes<MT, WT>& o, int g, bool valid) {
+  load_weights<MT, WT, Q>(f, rs, o, g, valid);
+  load_rest<MT, WT, Q>(f, rs, o, g, valid);
 }
 
 __device__ __forceinline__ void store_row4(_Float16* dst, float a0, float a1, float a2, float a3) {
@@ -141,22 +155,24 @@ __global__ __launch_bounds__(64 * WT * WK) void w4a16_skinny_kernel(
   __shared__ uint32_t lds[kTileWords > kRedWords ? kTileWords : kRedWords];
   auto xtile = [&](int buf, int slice) { return lds + (buf * WK + slice) * kXWords; };
 
-  f32x4 acc[MT][4];
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-    for (int c = 0; c < 4; ++c) acc[mt][c] = f32x4{0.f, 0.f, 0.f, 0.f};
-
+  // The first group's weights are requested before any other set-up: a
+  // freshly launched kernel fetches its instructions from L2, so every
+  // instruction ahead of a load delays it.
   Resources rs;
   rs.w = make_rsrc(pqw);
-  rs.z = make_rsrc(pqz);
-  rs.s = make_rsrc(psc);
-  rs.x = make_rsrc(px);
   const uint32_t N = (uint32_t)pN;
   Lanes<MT, WT> o;
   o.w = ((uint32_t)kb * N + col) * 4;
   o.wq = 16 * N;                                    // 4 packed rows
   o.gw = 64 * N;                                    // 16 packed rows
+  Frag<MT, WT, Q> f[D];
+  auto group_of = [&](int j) { return g0 + (j < n ? j : (n > 0 ? n - 1 : 0)); };
+  load_weights<MT, WT, Q>(f[0], rs, o, group_of(0), 0 < n);
+  __builtin_amdgcn_sched_barrier(0);
+
+  rs.z = make_rsrc(pqz);
+  rs.s = make_rsrc(psc);
+  rs.x = make_rsrc(px);
   o.z = (uint32_t)(col >> 3) * 4;
   o.gz = (N >> 3) * 4;
   o.s = (uint32_t)col * 2;
@@ -167,18 +183,23 @@ __global__ __launch_bounds__(64 * WT * WK) void w4a16_skinny_kernel(
     m = m < pM ? m : pM - 1;                        // rows past M: never stored
     o.x[q] = ((uint32_t)m * (uint32_t)pldx + chunk * 8) * 2;
   }
-  const uint32_t magic = in_vgpr(0x64006400u);
-  const int zshift = (lane & 1) * 16;
-
-  Frag<MT, WT, Q> f[D];
-  auto group_of = [&](int j) { return g0 + (j < n ? j : (n > 0 ? n - 1 : 0)); };
   // prologue loads in the loop's order (f[0] complete, then f[1], ...): the
   // wait counts at the loop head are then the same on entry and on the back edge
+  load_rest<MT, WT, Q>(f[0], rs, o, group_of(0), 0 < n);
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-  for (int i = 0; i < D; ++i) {
+  for (int i = 1; i < D; ++i) {
     load_group<MT, WT, Q>(f[i], rs, o, group_of(i), i < n);
     __builtin_amdgcn_sched_barrier(0);
   }
+  const uint32_t magic = in_vgpr(0x64006400u);
+  const int zshift = (lane & 1) * 16;
+
+  f32x4 acc[MT][4];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) acc[mt][c] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // One step per group: ring slot i (a compile-time index) is computed and
   // then refilled D groups ahead.  The loop body runs whole rounds of D
