@@ -125,7 +125,11 @@ __global__ __launch_bounds__(64 * WT * WK) void w4a16_skinny_kernel(
   constexpr int NW = WT * WK;                       // waves per block
   constexpr int kXWords = MT * 16 * kXRowWords;     // one group's activation tile
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  // the wave index is the same in every lane: read it into a scalar register,
+  // so that the wave's group range, its step count and the load masks derived
+  // from them are scalars (a per-lane value put the prologue's zero-point load
+  // under an exec-masked branch and every step's test on the vector ALU)
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wt = wave % WT, wk = wave / WT;
   const int cb = blockIdx.x;
   const int split = blockIdx.y;
