@@ -61,8 +61,7 @@ def cpu_baseline(wl, plan, drafts, min_seconds: float = 10.0):
     steps = 0
     t0 = time.perf_counter()
     while True:
-        ostep.verify_step(wl.x, wl.linears, plan, wl.lm_w, wl.lm_s, drafts, 1, drafts.shape[-1],
-                          workers=cores)
+        ostep.verify_step(wl.x, wl.linears, plan, wl.lm_w, wl.lm_s, drafts, 1, drafts.shape[-1])
         steps += 1
         if time.perf_counter() - t0 >= min_seconds:
             break

@@ -3,12 +3,12 @@
  *
  * The operations follow the organisers' page "Efficient LLM Challenge
  * Results" (adaptfm.gitlab.io/competition-results), section 3: a drafter
- * proposes K tokens, the target verifies them in a single forward pass over
- * the K+1 positions and keeps the longest prefix it would itself have
- * produced; the winning target is W4A16 GPTQ with group size 128 and an
- * untied lm_head quantised to 8 bits, served greedily; the runner-up pads
- * every draft to a constant K=20 with -1 sentinels, accepted only when they
- * match the target's own greedy token.  Section 5 names the W8A16 lm_head.
+ * proposes K tokens, one forward pass of the target over the K+1 positions
+ * checks them all, and the drafts are kept up to the first one that differs
+ * from the target's greedy token; the winning target is W4A16 GPTQ with group
+ * size 128 and an untied lm_head quantised to 8 bits, served greedily; the
+ * runner-up fills every draft up to a constant K=20 with -1, which can never
+ * equal a greedy token.  Section 5 names the W8A16 lm_head.
  *
  * Conventions for every call:
  *   - Tensor pointers are DEVICE pointers owned by the caller.  The library

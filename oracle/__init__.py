@@ -7,12 +7,12 @@ binding) never does, and this package never imports the product path.  The
 two sides share nothing but the seeded input module ``gen``.
 
 Sources (organisers' page "Efficient LLM Challenge Results", adaptfm.gitlab.io):
-  section 3  -- speculative decoding: K drafts verified in one target pass,
-                keep the longest prefix the target would itself produce;
-                greedy serving; the winner's target is W4A16 GPTQ with group
-                size 128 and an untied lm_head quantised to 8 bits; the
-                runner-up pads drafts to K=20 with -1 sentinels, and a padded
-                position is accepted only if it equals the target's greedy token.
+  section 3  -- speculative decoding: one target pass checks K drafts,
+                which are kept up to the first that differs from the target's
+                greedy token; greedy serving; the winner's target is W4A16 GPTQ
+                with group size 128 and an untied lm_head quantised to 8 bits;
+                the runner-up fills drafts up to K=20 with -1, which never
+                matches a vocabulary id.
                 Table 3 and the paragraph on n-gram drafting: the prompt-
                 lookup drafter copies spans from the prompt, no auxiliary
                 model, fixed K (23 for the team that used it).
@@ -33,7 +33,7 @@ Modules:
 Every function is pinned by a ``-m "not gpu"`` test (pack/unpack round trips,
 hand-built words, identity and one-hot weights, closed forms, exact-rational
 brute force on tiny shapes, exhaustive enumeration for the verify and the
-drafter).  No
-function here is "parity unpinned".
+drafter; the chain of ``step`` by permutation chains with mixed widths and
+hand-worked rounding cases in ``tests/test_oracle_step.py``).
 """
 from . import quant, gemm, lmhead, verify, step, ngram, gdn  # noqa: F401

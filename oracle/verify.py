@@ -1,11 +1,12 @@
 """Greedy prefix acceptance (oracle; test infrastructure only).
 
-Results page, section 3: the target verifies K drafted tokens in one forward
-pass and keeps the longest prefix it would itself have produced; under greedy
-verification the output is unchanged whatever the drafts are.  Drafts padded
-to a constant K with -1 sentinels stay lossless because a padded position is
-accepted only when it equals the target's own greedy token -- which a -1
-never does.
+Results page ("Efficient LLM Challenge Results", section 3): one forward pass
+of the target checks all K drafts, and the drafts survive up to the first one
+that differs from the target's own greedy choice at that position; with greedy
+decoding this leaves the emitted text exactly what the target alone would
+write.  The runner-up fills short drafts up to a fixed K with -1; since -1 is
+no vocabulary id, a filler can never match, and the padding cannot change what
+is accepted.
 
 Row j of sequence b's target ids (j = 0..K) is the target's greedy token after
 consuming the current token and drafts 0..j-1.  The accepted length a is the

@@ -50,14 +50,15 @@ def stagewise(step, wl, sample_cols=None, seed=0):
     return host(h)
 
 
-def free_running(wl, step, oracle_workers=8):
-    """G3: drafts from the oracle's own free-running target ids (fresh draft stream)."""
+def free_running(wl, step, min_pinned=1):
+    """G3: drafts from the oracle's own free-running target ids (fresh draft stream).
+    At least ``min_pinned`` sequences must have every consulted row above the
+    margin, so that the comparison decides something."""
     import torch
     cfg = wl.cfg
     plan = gen.chain_plan(cfg)
     ref = ostep.verify_step(wl.x, wl.linears, plan, wl.lm_w, wl.lm_s,
-                            np.zeros((cfg.batch, cfg.k_draft), np.int32), cfg.batch, cfg.k_draft,
-                            workers=oracle_workers)
+                            np.zeros((cfg.batch, cfg.k_draft), np.int32), cfg.batch, cfg.k_draft)
     t_o, margin = ref["target_ids"], ref["margin"]
     drafts, r = gen.make_drafts(gen.draft_rng(cfg.cid), cfg, t_o)
     a_o, out_o = over.greedy_verify(t_o.reshape(cfg.batch, -1), drafts, cfg.vocab)
@@ -81,6 +82,7 @@ def free_running(wl, step, oracle_workers=8):
             assert np.array_equal(out[b][:upto], out_o[b][:upto])
     log(f"  free-running: final-h rel-L2 {rel_h:.2e}; {pinned}/{cfg.batch} sequences pinned; "
         f"accepted {acc.tolist()} (oracle {a_o.tolist()})")
+    assert pinned >= min_pinned, f"only {pinned} of {cfg.batch} sequences pinned"
     return pinned
 
 
@@ -93,7 +95,7 @@ def test_c1_block_linear_step(lib):
     t_g, _ = lib.w8a16_lmhead_argmax(dev(h), step.lm_w, step.lm_s)
     torch.cuda.synchronize()
     check_argmax(host(t_g), lg, "c1 lm_head")
-    assert free_running(wl, step) >= 0
+    free_running(wl, step)
 
 
 def test_c2_decode_layer(lib):
@@ -114,8 +116,8 @@ def test_c3_verify_step(lib):
     log("c3: generating inputs")
     wl = gen.make_workload(3)
     step = device_step(wl)
-    log("c3: stage-wise (sampled columns)")
-    h = stagewise(step, wl, sample_cols=64, seed=3)
+    log("c3: stage-wise (every output column of all 144 linears)")
+    h = stagewise(step, wl)
     lg = olm.logits(h, wl.lm_w, wl.lm_s)
     import torch
     t_g, _ = lib.w8a16_lmhead_argmax(dev(h), step.lm_w, step.lm_s)
