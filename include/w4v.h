@@ -252,37 +252,43 @@ int gdn_state_commit(float* state, const float* k, const float* v, const float* 
  * with W_l in the layout of w4a16_gemm.  Each intermediate output is rounded
  * to fp16 exactly as a separate w4a16_gemm call would round it.
  *
- * One block per compute unit stays resident for the whole chain; the plan
- * gives every linear at most one unit (64, 128 or 256 output columns x one
- * K-split) per block.  A unit of linear l waits only for the 64-column
- * tiles of linear l-1's output that it reads (per-tile ready flags in the
- * workspace), and a block starts streaming its next unit's weights while the
- * current unit is reduced and published.
+ * One block per compute unit stays resident for the whole chain.  Each
+ * linear's output columns are dealt to eight groups of blocks (one per XCD:
+ * the hardware deals blocks round-robin over the XCDs) and, inside a group,
+ * to units of 16-80 columns x one K-split; every block's units are copied,
+ * in chain order, into one contiguous stream in the workspace (the same
+ * bytes as the canonical layout, reordered), which the block streams into
+ * LDS ahead of the math.  A unit of linear l waits only for the output tiles
+ * of linear l-1 it reads (ready flags in the workspace); split-K partial sums
+ * stay in the group's L2 when all of a group's blocks report the same XCD.
  *
- * w4a16_chain_prepare writes the launch plan (per-linear descriptors,
- * buffers) for the current device's compute-unit count into the
- * caller's workspace with synchronous copies; it must not run while a call
- * that uses this workspace is in flight.  The prepared workspace is then used
- * by any number of w4a16_chain calls ordered on one stream, on the same
- * device (also from a captured graph: each launch leaves the buffers the
- * next launch writes in their prepared state).
- * The linears' device arrays must stay valid and unchanged.
+ * w4a16_chain_prepare writes the launch plan for the current device's
+ * compute-unit count into the caller's workspace and copies every linear's
+ * weights, scales and zero-points into it (stream-ordered kernels, then a
+ * device synchronisation); it must not run while a call that uses this
+ * workspace is in flight.  After it returns, the linears' own device arrays
+ * are no longer read.  The prepared workspace is then used by any number of
+ * w4a16_chain calls ordered on one stream, on the same device (also from a
+ * captured graph: each launch leaves the buffers the next launch writes in
+ * their prepared state).
  *
  * linears    host array of n_linears descriptors (device pointers inside),
  *            1 <= n_linears <= 65535; K % 128 == 0, N % 8 == 0, qweight and
- *            scales 16-byte aligned, qzeros 4-byte aligned; K*N/2 below
- *            2 GiB and N at most 256 columns per compute unit
- *            (W4V_ERR_UNSUPPORTED otherwise).
+ *            qzeros 4-byte aligned, scales 2-byte aligned; N % 16 != 0, or a
+ *            linear the plan cannot fit in one block's LDS ring and registers
+ *            (more than 24 groups of 128 k per unit, more than 64 input tiles
+ *            per unit), returns W4V_ERR_UNSUPPORTED.
  * M          1..16 rows (W4V_ERR_UNSUPPORTED above 16).
  * x          fp16 [M x K_0], row stride ldx >= K_0, 16-byte aligned, ldx % 8 == 0.
  * y          fp16 [M x N_{n-1}], row stride ldy >= N_{n-1}, 16-byte aligned,
  *            ldy % 8 == 0; must not overlap x.
- * workspace  w4a16_chain_workspace_size(...) bytes, 256-byte aligned.  Byte
- *            offset 28 holds an error word the kernel sets (sticky until the
- *            caller clears it): 1 = a wait for another block's output exceeded its bound
- *            (results invalid; the workspace must be prepared again),
- *            2 = the workspace was not prepared for this M, K_0, N_{n-1} and
- *            device, or a previous call gave up a wait (nothing computed).
+ * workspace  w4a16_chain_workspace_size(...) bytes (about the linears' own
+ *            bytes plus their outputs and partial sums), 256-byte aligned.
+ *            Byte offset 28 holds an error word the kernel sets (sticky until
+ *            the caller prepares again): 1 = a wait for another block's output
+ *            exceeded its bound (results invalid), 2 = the workspace was not
+ *            prepared for this M, K_0, N_{n-1} and device, or a previous call
+ *            gave up a wait (nothing computed).
  * Each output element is computed in a fixed order, so results are
  * bit-identical from call to call.
  * ---------------------------------------------------------------------- */

@@ -11,12 +11,10 @@ from tests.gpu_util import check_gemm, dev, host, log
 
 pytestmark = pytest.mark.gpu
 
-# ChainLinear (w4v_launch.h): 7 pointers, 6 ints, float, int
-_LIN = np.dtype([("qweight", "<u8"), ("scales", "<u8"), ("qzeros", "<u8"), ("out", "<u8"),
-                 ("partials", "<u8"), ("tickets", "<u8"), ("flags", "<u8"), ("K", "<i4"),
-                 ("N", "<i4"), ("ldo", "<i4"),
-                 ("splits", "<i4"), ("cb", "<i4"), ("units", "<i4"), ("alpha", "<f4"),
-                 ("wt", "<i4")])
+# ChainLinear (w4v_launch.h): 4 pointers, 3 ints, float, 4 ints
+_LIN = np.dtype([("out", "<u8"), ("flags", "<u8"), ("sflags", "<u8"), ("partials", "<u8"),
+                 ("K", "<i4"), ("N", "<i4"), ("ldo", "<i4"), ("alpha", "<f4"),
+                 ("S", "<i4"), ("tiles", "<i4"), ("pad0", "<i4"), ("pad1", "<i4")])
 
 
 def intermediates(chain):
@@ -67,7 +65,7 @@ def check_chain(chain, x, lins, alphas, y, sample_cols=None, seed=0):
 @pytest.mark.parametrize("m", [16, 1, 5])
 def test_chain_small(lib, m):
     rng = np.random.default_rng(100 + m)
-    shapes = [(256, 200), (128, 1024), (1024, 640), (640, 136), (128, 2560)]
+    shapes = [(256, 208), (128, 1024), (1024, 640), (640, 144), (128, 2560)]
     lins = [gen.qlinear(rng, k, n) for k, n in shapes]
     alphas = [gen.chain_alpha(k) for k, _ in shapes]
     x = gen.activations(rng, m, shapes[0][0])
@@ -88,8 +86,8 @@ def test_chain_single_linear(lib):
 
 
 def test_chain_verify_step_layers(lib):
-    """The 36-layer verify-step chain at M = 16: all 144 linears stage-wise (sampled columns),
-    bit-identical repeats, error word clear after several launches."""
+    """The 36-layer verify-step chain at M = 16: all 144 linears stage-wise (every output
+    column), bit-identical repeats, error word clear after several launches."""
     import torch
     log("chain c3: generating")
     wl = gen.make_workload(3, vocab=0)
@@ -105,7 +103,7 @@ def test_chain_verify_step_layers(lib):
     assert chain.error() == 0
     assert np.array_equal(y1.view(np.uint16), y2.view(np.uint16))
     assert np.array_equal(y1.view(np.uint16), y3.view(np.uint16))
-    worst = check_chain(chain, wl.x, lins, alphas, y3, sample_cols=64, seed=5)
+    worst = check_chain(chain, wl.x, lins, alphas, y3)
     log(f"  chain c3: worst stage-wise rel-L2 {worst:.2e} over {len(lins)} linears")
 
 

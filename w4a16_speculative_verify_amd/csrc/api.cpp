@@ -6,6 +6,7 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <algorithm>
 #include <vector>
 
 #include "w4v.h"
@@ -96,41 +97,46 @@ int run_lmhead(const void* h, int64_t ldh, const void* w, const void* scales, in
   return e == hipSuccess ? W4V_OK : W4V_ERR_HIP;
 }
 
-// Unit shape of linear (K, N) for a grid of `blocks` blocks: wt 64-column
-// tiles per column block and S K-splits, with cb * S <= blocks and every
-// unit's activation slice fitting in LDS.  Among the shapes that fit, the one
-// with the least estimated time: the slowest block's weight stream (at most
-// one compute unit's share of the load bandwidth, and never faster than the
-// whole linear at the HBM rate), its activation slice, and for S > 1 the
-// round trips of the split hand-off plus the last split's read of the
-// partials.  Returns false when no shape fits.
-struct ChainShape { int wt, splits; };
-bool chain_shape(int K, int N, int blocks, ChainShape* out) {
-  constexpr double kCuBytesPerNs = 50.0;      // one CU streaming alone
-  constexpr double kHbmBytesPerNs = 7000.0;   // the whole chip
-  constexpr double kL2BytesPerNs = 100.0;     // one CU reading activations
-  constexpr double kSplitNs = 1500.0;         // partial store, ticket, partial loads
-  const int G = K / w4v::kGroup;
-  const int T = (N + w4v::kColTile - 1) / w4v::kColTile;
-  const double total = (double)K * N / 2;
+// ---------------------------------------------------------------- chain plan
+// Linear l's 16-column blocks are dealt to G groups of blocks (G = 8 when the
+// block count allows: block b belongs to group b % G, the XCD the hardware
+// deals it to), contiguously; inside a group, tiles of nb column blocks x S
+// K-splits give one unit per block.  nb and S are chosen per linear by a small
+// estimate of the slowest unit's time after its inputs are ready: its weights
+// through dequantisation and MFMA (about 55 KB/us per CU), its activation rows
+// from L2 (about 150 KB/us), and for S > 1 the split hand-off (about 0.8 us)
+// plus the last split's read of the partials.
+struct ChainPlan {
+  int blocks = 0, G = 1, P = 0, n = 0;
+  std::vector<w4v::ChainUnit> units;          // [n][blocks]
+  std::vector<int> S, tiles, max_ng, N;
+  std::vector<std::vector<int>> tile_c0;      // per linear: first column of each tile (+ end)
+  std::vector<size_t> part_floats;            // per linear
+  std::vector<uint64_t> stream_bytes;         // per block
+  size_t lin_offset = 0, unit_offset = 0, stream_offset = 0, xcc_offset = 0;
+  size_t counters_offset = 0, buffers_offset = 0, streams_base = 0, bytes = 0;
+  std::vector<size_t> flag_off, sflag_off, out_off, part_off;
+  std::vector<uint64_t> stream_off;
+};
+
+bool chain_shape(int Gk, int nbx_max, int P, int* nb_out, int* S_out) {
+  constexpr double kComputeKBperUs = 55.0, kL2KBperUs = 150.0, kSplitUs = 0.8;
+  const int ring_kb = w4v::kChainRingBytes / 1024;
   double best = 0;
   bool found = false;
-  for (int wt = 1; wt <= 4; wt *= 2) {
-    const int cb = (T + wt - 1) / wt;
-    if (cb > blocks) continue;
-    const int s_max = blocks / cb < G ? blocks / cb : G;
-    for (int S = 1; S <= s_max; ++S) {
-      const int glen = (G + S - 1) / S;
-      if (glen > w4v::kChainMaxGroups) continue;
-      const double wbytes = (double)glen * wt * w4v::kColTile * w4v::kGroup / 2;
-      const double xbytes = (double)glen * 16 * w4v::kGroup * 2;
-      double t = wbytes / kCuBytesPerNs;
-      if (t < total / kHbmBytesPerNs) t = total / kHbmBytesPerNs;
-      t += xbytes / kL2BytesPerNs;
-      if (S > 1) t += kSplitNs + (double)S * wt * 16 * w4v::kColTile * 4 / kCuBytesPerNs;
-      if (!found || t < best) {
+  for (int nb = 1; nb <= w4v::kChainMaxNb; ++nb) {
+    const int T = (nbx_max + nb - 1) / nb;
+    for (int S = 1; S <= Gk && T * S <= P; ++S) {
+      const int ngmax = (Gk + S - 1) / S;
+      if (ngmax > w4v::kChainComputeWaves * w4v::kChainMaxWaveGroups) continue;
+      const double unit_bytes = (double)ngmax * w4v::chain_group_bytes(nb);
+      if ((1023.0 + unit_bytes) / 1024.0 > ring_kb) continue;
+      double t = unit_bytes / 1024.0 / kComputeKBperUs + 4.0 * ngmax / kL2KBperUs;
+      if (S > 1) t += kSplitUs + (double)S * nb / kL2KBperUs;
+      if (!found || t < best - 1e-9) {
         best = t;
-        *out = ChainShape{wt, S};
+        *nb_out = nb;
+        *S_out = S;
         found = true;
       }
     }
@@ -138,64 +144,130 @@ bool chain_shape(int K, int N, int blocks, ChainShape* out) {
   return found;
 }
 
-// Workspace bytes of linear l's ready flags (one word per 64-column tile),
-// split tickets, output (16 rows; none for the last linear) and split
-// partials.
-size_t chain_flag_bytes(int N) {
-  const int T = (N + w4v::kColTile - 1) / w4v::kColTile;
-  return w4v::align_up((size_t)T * sizeof(unsigned), 256);
-}
-size_t chain_out_bytes(int N) {
-  const int T = (N + w4v::kColTile - 1) / w4v::kColTile;
-  return w4v::align_up(16 * (size_t)T * w4v::kColTile * 2, 256);
-}
-size_t chain_ticket_bytes(int N, const ChainShape& sh) {
-  const int T = (N + w4v::kColTile - 1) / w4v::kColTile;
-  const int cb = (T + sh.wt - 1) / sh.wt;
-  return sh.splits == 1 ? 0 : (size_t)cb * sh.wt * w4v::kChainSlot;
-}
-size_t chain_partial_bytes(int N, const ChainShape& sh) {
-  const int T = (N + w4v::kColTile - 1) / w4v::kColTile;
-  const int cb = (T + sh.wt - 1) / sh.wt;
-  if (sh.splits == 1) return 0;
-  return w4v::align_up((size_t)sh.splits * 16 * cb * sh.wt * w4v::kColTile * 4, 256);
-}
-
-// Checks the descriptors and lays out the workspace for a grid of `blocks`:
-// header, descriptor table, ready flags and tickets (zeroed by prepare), then
-// the intermediate outputs and split partials.  Host-only.
-int chain_layout(const w4v_chain_linear* lins, int n, int M, int blocks, w4v::ChainLayout* lay) {
+int chain_plan(const w4v_chain_linear* lins, int n, int M, int blocks, ChainPlan* p) {
   if (!lins || n < 1 || n > 65535) return W4V_ERR_INVALID_ARG;
   if (M < 1) return W4V_ERR_INVALID_ARG;
   if (M > w4v::kChainMaxRows) return W4V_ERR_UNSUPPORTED;
   if (blocks < 1) return W4V_ERR_HIP;
-  size_t off = sizeof(w4v::ChainHeader);
-  lay->lin_offset = off;
-  off += w4v::align_up((size_t)n * sizeof(w4v::ChainLinear), 256);
-  ChainShape sh{};
+  p->blocks = blocks;
+  p->G = blocks % w4v::kChainGroups == 0 ? w4v::kChainGroups : 1;
+  p->P = blocks / p->G;
+  p->n = n;
+  p->units.assign((size_t)n * blocks, w4v::ChainUnit{-1, 0, 0, 0, 0, 1, 0, 0, 0, 0u, 0, 0u});
+  p->S.assign(n, 1);
+  p->tiles.assign(n, 0);
+  p->max_ng.assign(n, 0);
+  p->N.assign(n, 0);
+  p->tile_c0.assign(n, {});
+  p->part_floats.assign(n, 0);
+  p->stream_bytes.assign(blocks, 0);
   for (int l = 0; l < n; ++l) {
     const w4v_chain_linear& L = lins[l];
     if (L.K <= 0 || L.N <= 0 || L.K % w4v::kGroup != 0 || L.N % 8 != 0) return W4V_ERR_INVALID_ARG;
+    if (L.N % 16 != 0) return W4V_ERR_UNSUPPORTED;
     if (l > 0 && L.K > lins[l - 1].N) return W4V_ERR_INVALID_ARG;
     if (!L.qweight || !L.scales || !L.qzeros) return W4V_ERR_INVALID_ARG;
-    if (!aligned(L.qweight, 16) || !aligned(L.scales, 16) || !aligned(L.qzeros, 4))
+    if (!aligned(L.qweight, 4) || !aligned(L.scales, 2) || !aligned(L.qzeros, 4))
       return W4V_ERR_ALIGNMENT;
-    // buffer resources take 32-bit offsets below 2 GiB
-    if ((size_t)L.K * L.N / 2 >= (1ull << 31)) return W4V_ERR_UNSUPPORTED;
-    if (!chain_shape(L.K, L.N, blocks, &sh)) return W4V_ERR_UNSUPPORTED;
+    const int Gk = L.K / w4v::kGroup, NB = L.N / 16;
+    const int nbx_max = (NB + p->G - 1) / p->G;
+    int nb = 0, S = 0;
+    if (!chain_shape(Gk, nbx_max, p->P, &nb, &S)) return W4V_ERR_UNSUPPORTED;
+    p->S[l] = S;
+    p->N[l] = L.N;
+    int tile = 0;
+    size_t pf = 0;
+    for (int x = 0; x < p->G; ++x) {
+      const int cb_lo = (int)((long)NB * x / p->G), cb_hi = (int)((long)NB * (x + 1) / p->G);
+      const int T = (cb_hi - cb_lo + nb - 1) / nb;
+      for (int t = 0; t < T; ++t, ++tile) {
+        const int c_lo = cb_lo + t * nb;
+        const int nbt = std::min(nb, cb_hi - c_lo);
+        p->tile_c0[l].push_back(c_lo * 16);
+        for (int sp = 0; sp < S; ++sp) {
+          const int b = x + p->G * (t * S + sp);
+          w4v::ChainUnit& U = p->units[(size_t)l * blocks + b];
+          U.col0 = c_lo * 16;
+          U.nb = nbt;
+          U.g0 = Gk * sp / S;
+          U.ng = Gk * (sp + 1) / S - U.g0;
+          U.split = sp;
+          U.S = S;
+          U.tile = tile;
+          U.gbytes = w4v::chain_group_bytes(nbt);
+          U.soff = (unsigned)p->stream_bytes[b];
+          U.part_off = (int)pf;
+          p->stream_bytes[b] += (uint64_t)U.ng * U.gbytes;
+          if (p->stream_bytes[b] >= (1ull << 31)) return W4V_ERR_UNSUPPORTED;
+          p->max_ng[l] = std::max(p->max_ng[l], U.ng);
+        }
+        if (S > 1) pf += (size_t)(S - 1) * 16 * nbt * 16;
+      }
+    }
+    p->tile_c0[l].push_back(L.N);
+    p->tiles[l] = tile;
+    p->part_floats[l] = pf;
   }
-  lay->counters_offset = off;
+  // the input tiles of every unit: tiles of linear l-1 whose columns meet the
+  // unit's k-range
+  for (int l = 1; l < n; ++l) {
+    const std::vector<int>& c0 = p->tile_c0[l - 1];
+    const int T = p->tiles[l - 1];
+    for (int b = 0; b < blocks; ++b) {
+      w4v::ChainUnit& U = p->units[(size_t)l * blocks + b];
+      if (U.col0 < 0) continue;
+      const int k0 = U.g0 * w4v::kGroup, k1 = (U.g0 + U.ng) * w4v::kGroup;
+      int f0 = 0;
+      while (f0 < T && c0[f0 + 1] <= k0) ++f0;
+      int f1 = f0;
+      while (f1 < T && c0[f1] < k1) ++f1;
+      U.f0 = f0;
+      U.nf = f1 - f0;
+      if (U.nf > w4v::kChainMaxFlags) return W4V_ERR_UNSUPPORTED;
+    }
+  }
+  // layout: header, tables, counters (zeroed by prepare), buffers, streams
+  size_t off = sizeof(w4v::ChainHeader);
+  p->lin_offset = off;
+  off += w4v::align_up((size_t)n * sizeof(w4v::ChainLinear), 256);
+  p->unit_offset = off;
+  off += w4v::align_up((size_t)n * blocks * sizeof(w4v::ChainUnit), 256);
+  p->stream_offset = off;
+  off += w4v::align_up((size_t)blocks * sizeof(w4v::ChainStream), 256);
+  p->counters_offset = off;
+  p->xcc_offset = off;
+  off += w4v::align_up((size_t)blocks * sizeof(unsigned), 256);
+  p->flag_off.assign(n, 0);
+  p->sflag_off.assign(n, 0);
+  p->out_off.assign(n, 0);
+  p->part_off.assign(n, 0);
   for (int l = 0; l < n; ++l) {
-    chain_shape(lins[l].K, lins[l].N, blocks, &sh);
-    off += chain_flag_bytes(lins[l].N) + chain_ticket_bytes(lins[l].N, sh);
+    p->flag_off[l] = off;
+    off += w4v::align_up((size_t)p->tiles[l] * sizeof(unsigned), 256);
+    if (p->S[l] > 1) {
+      p->sflag_off[l] = off;
+      off += w4v::align_up((size_t)p->tiles[l] * p->S[l] * sizeof(unsigned), 256);
+    }
   }
-  lay->buffers_offset = off;
+  p->buffers_offset = off;
   for (int l = 0; l < n; ++l) {
-    chain_shape(lins[l].K, lins[l].N, blocks, &sh);
-    if (l < n - 1) off += chain_out_bytes(lins[l].N);
-    off += chain_partial_bytes(lins[l].N, sh);
+    if (l < n - 1) {
+      p->out_off[l] = off;
+      off += w4v::align_up((size_t)16 * p->N[l] * 2, 256);
+    }
+    if (p->S[l] > 1) {
+      p->part_off[l] = off;
+      off += w4v::align_up(p->part_floats[l] * sizeof(float), 256);
+    }
   }
-  lay->bytes = off;
+  off = w4v::align_up(off, 1024);
+  p->streams_base = off;
+  p->stream_off.assign(blocks, 0);
+  for (int b = 0; b < blocks; ++b) {
+    p->stream_off[b] = off;
+    off += w4v::align_up(p->stream_bytes[b], 1024);
+  }
+  p->bytes = off;
   return W4V_OK;
 }
 
@@ -462,21 +534,21 @@ int append_accepted(int32_t* history, int64_t ld, int32_t* lengths, int B, int K
 }
 
 size_t w4a16_chain_workspace_size(const w4v_chain_linear* linears, int n_linears, int M) {
-  w4v::ChainLayout lay{};
-  if (chain_layout(linears, n_linears, M, chain_blocks(), &lay) != W4V_OK) return 0;
-  return lay.bytes;
+  ChainPlan p;
+  if (chain_plan(linears, n_linears, M, chain_blocks(), &p) != W4V_OK) return 0;
+  return p.bytes;
 }
 
 int w4a16_chain_prepare(const w4v_chain_linear* linears, int n_linears, int M, void* workspace,
                         size_t workspace_bytes) {
   const int blocks = chain_blocks();
-  w4v::ChainLayout lay{};
-  int st = chain_layout(linears, n_linears, M, blocks, &lay);
+  ChainPlan p;
+  int st = chain_plan(linears, n_linears, M, blocks, &p);
   if (st != W4V_OK) return st;
-  if (!workspace || workspace_bytes < lay.bytes) return W4V_ERR_WORKSPACE;
+  if (!workspace || workspace_bytes < p.bytes) return W4V_ERR_WORKSPACE;
   if (!aligned(workspace, 256)) return W4V_ERR_ALIGNMENT;
   char* base = static_cast<char*>(workspace);
-  std::vector<char> img(lay.counters_offset, 0);
+  std::vector<char> img(p.counters_offset, 0);
   w4v::ChainHeader* hdr = reinterpret_cast<w4v::ChainHeader*>(img.data());
   hdr->magic = w4v::kChainMagic;
   hdr->n_linears = (unsigned)n_linears;
@@ -484,48 +556,51 @@ int w4a16_chain_prepare(const w4v_chain_linear* linears, int n_linears, int M, v
   hdr->M = (unsigned)M;
   hdr->K0 = (unsigned)linears[0].K;
   hdr->N_last = (unsigned)linears[n_linears - 1].N;
-  hdr->lin_offset = lay.lin_offset;
-  w4v::ChainLinear* tab = reinterpret_cast<w4v::ChainLinear*>(img.data() + lay.lin_offset);
-  size_t cnt_off = lay.counters_offset;
-  size_t buf_off = lay.buffers_offset;
+  hdr->groups = (unsigned)p.G;
+  hdr->group_blocks = (unsigned)p.P;
+  hdr->lin_offset = p.lin_offset;
+  hdr->unit_offset = p.unit_offset;
+  hdr->stream_offset = p.stream_offset;
+  hdr->xcc_offset = p.xcc_offset;
+  w4v::ChainLinear* tab = reinterpret_cast<w4v::ChainLinear*>(img.data() + p.lin_offset);
   for (int l = 0; l < n_linears; ++l) {
-    const w4v_chain_linear& L = linears[l];
     w4v::ChainLinear& d = tab[l];
-    const int T = (L.N + w4v::kColTile - 1) / w4v::kColTile;
-    ChainShape sh{};
-    chain_shape(L.K, L.N, blocks, &sh);
-    const int cb = (T + sh.wt - 1) / sh.wt;
-    d.qweight = reinterpret_cast<const uint32_t*>(L.qweight);
-    d.scales = static_cast<const _Float16*>(L.scales);
-    d.qzeros = reinterpret_cast<const uint32_t*>(L.qzeros);
-    d.K = L.K;
-    d.N = L.N;
-    d.wt = sh.wt;
-    d.cb = cb;
-    d.splits = sh.splits;
-    d.units = cb * sh.splits;
-    d.alpha = L.alpha;
-    d.ldo = T * w4v::kColTile;
-    d.flags = reinterpret_cast<unsigned*>(base + cnt_off);
-    cnt_off += chain_flag_bytes(L.N);
-    d.tickets = reinterpret_cast<unsigned*>(base + cnt_off);
-    cnt_off += chain_ticket_bytes(L.N, sh);
-    d.out = nullptr;
-    if (l < n_linears - 1) {
-      d.out = reinterpret_cast<_Float16*>(base + buf_off);
-      buf_off += chain_out_bytes(L.N);
-    }
-    d.partials = nullptr;
-    if (sh.splits > 1) {
-      d.partials = reinterpret_cast<float*>(base + buf_off);
-      buf_off += chain_partial_bytes(L.N, sh);
-    }
+    d.out = l < n_linears - 1 ? reinterpret_cast<_Float16*>(base + p.out_off[l]) : nullptr;
+    d.flags = reinterpret_cast<unsigned*>(base + p.flag_off[l]);
+    d.sflags = p.S[l] > 1 ? reinterpret_cast<unsigned*>(base + p.sflag_off[l]) : nullptr;
+    d.partials = p.S[l] > 1 ? reinterpret_cast<float*>(base + p.part_off[l]) : nullptr;
+    d.K = linears[l].K;
+    d.N = linears[l].N;
+    d.ld_out = linears[l].N;
+    d.alpha = linears[l].alpha;
+    d.S = p.S[l];
+    d.tiles = p.tiles[l];
+  }
+  memcpy(img.data() + p.unit_offset, p.units.data(), p.units.size() * sizeof(w4v::ChainUnit));
+  w4v::ChainStream* sts = reinterpret_cast<w4v::ChainStream*>(img.data() + p.stream_offset);
+  for (int b = 0; b < blocks; ++b) {
+    sts[b].offset = p.stream_off[b];
+    sts[b].kb = (unsigned)(w4v::align_up(p.stream_bytes[b], 1024) / 1024);
+    sts[b].pad = 0;
   }
   if (hipMemcpy(workspace, img.data(), img.size(), hipMemcpyHostToDevice) != hipSuccess)
     return W4V_ERR_HIP;
-  if (hipMemset(base + lay.counters_offset, 0, lay.buffers_offset - lay.counters_offset) !=
-      hipSuccess)
+  if (hipMemset(base + p.counters_offset, 0, p.buffers_offset - p.counters_offset) != hipSuccess)
     return W4V_ERR_HIP;
+  // the streams' tails past the last unit are never computed on; zero them
+  // anyway so that every byte the loader copies is defined
+  if (hipMemset(base + p.streams_base, 0, p.bytes - p.streams_base) != hipSuccess)
+    return W4V_ERR_HIP;
+  for (int l = 0; l < n_linears; ++l) {
+    if (p.max_ng[l] == 0) continue;
+    hipError_t e = w4v::launch_w4a16_chain_prepack(
+        reinterpret_cast<const w4v::ChainUnit*>(base + p.unit_offset) + (size_t)l * blocks,
+        reinterpret_cast<const w4v::ChainStream*>(base + p.stream_offset), blocks, p.max_ng[l],
+        reinterpret_cast<const uint32_t*>(linears[l].qweight),
+        static_cast<const _Float16*>(linears[l].scales),
+        reinterpret_cast<const uint32_t*>(linears[l].qzeros), linears[l].N, base, nullptr);
+    if (e != hipSuccess) return W4V_ERR_HIP;
+  }
   if (hipDeviceSynchronize() != hipSuccess) return W4V_ERR_HIP;
   return W4V_OK;
 }
@@ -538,6 +613,8 @@ int w4a16_chain(const void* x, int64_t ldx, void* y, int64_t ldy, int M, int K0,
   if (ldx < K0 || ldy < N_last) return W4V_ERR_INVALID_ARG;
   if (!aligned(x, 16) || ldx % 8 != 0 || !aligned(y, 16) || ldy % 8 != 0 || !aligned(workspace, 256))
     return W4V_ERR_ALIGNMENT;
+  if ((size_t)M * (size_t)ldx * 2 >= (1ull << 31) || (size_t)M * (size_t)ldy * 2 >= (1ull << 31))
+    return W4V_ERR_UNSUPPORTED;
   const size_t xbytes = ((size_t)(M - 1) * (size_t)ldx + (size_t)K0) * 2;
   const size_t ybytes = ((size_t)(M - 1) * (size_t)ldy + (size_t)N_last) * 2;
   if (ranges_overlap(x, xbytes, y, ybytes)) return W4V_ERR_INVALID_ARG;

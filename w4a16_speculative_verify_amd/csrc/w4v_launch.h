@@ -103,12 +103,26 @@ hipError_t launch_lmhead_argmax(const LmheadArgs& a, const LmheadPlan& p, void* 
                                 hipStream_t stream);
 
 // ---------------------------------------------------------------- chain of linears
-constexpr unsigned kChainMagic = 0x37435734u;   // "4WC7"
-constexpr int kChainComputeWaves = 4;           // tiles x k-slices of a unit
-constexpr int kChainThreads = 64 * (kChainComputeWaves + 1);   // + one control wave
-constexpr int kChainMaxGroups = 24;             // 128-k groups of one unit's activation slice (LDS)
+// One persistent launch for a chain of W4A16 linears at M <= 16 rows.  Each
+// block's share of every linear (its "unit": nb 16-column blocks x ng 128-k
+// groups) is prepacked, in chain order, into one contiguous byte stream per
+// block, which a loader wave copies into an LDS ring ahead of the math.
+constexpr unsigned kChainMagic = 0x32435734u;   // "4WC2"
+constexpr int kChainComputeWaves = 8;           // two per SIMD
+constexpr int kChainThreads = 64 * (kChainComputeWaves + 1);   // + the loader wave
+constexpr int kChainRingBytes = 112 * 1024;     // LDS ring of the weight stream (multiple of 1 KiB)
+constexpr int kChainMaxNb = 5;                  // 16-column blocks per unit
+constexpr int kChainMaxWaveGroups = 3;          // 128-k groups per compute wave (A in registers)
 constexpr int kChainMaxRows = 16;
-constexpr size_t kChainSlot = 256;              // bytes per ticket (one cache line or more)
+constexpr int kChainMaxFlags = 64;              // input tiles one unit may wait for
+constexpr int kChainGroups = 8;                 // blocks dealt round-robin over the XCDs
+
+// bytes of one 128-k group of a unit of nb column blocks in the stream:
+// nb x 1 KiB of packed words (lane-ordered), then nb*16 fp16 scales and
+// 2*nb zero-point words, padded to 16 bytes
+inline constexpr unsigned chain_group_bytes(int nb) {
+  return (unsigned)nb * 1024u + (unsigned)((40 * nb + 15) / 16 * 16);
+}
 
 // Device-side header at offset 0 of a prepared chain workspace (256 bytes).
 struct ChainHeader {
@@ -122,39 +136,55 @@ struct ChainHeader {
   unsigned error;        // byte offset 28: 1 a wait timed out, 2 workspace not prepared for this call
   unsigned K0;           // width of the input rows
   unsigned N_last;       // width of the output rows
-  unsigned pad0[2];
-  uint64_t lin_offset;   // byte offset of the ChainLinear table
-  uint64_t pad1;
-  unsigned pad2[48];
+  unsigned groups;       // block groups (kChainGroups, or 1)
+  unsigned group_blocks; // blocks per group
+  uint64_t lin_offset;   // byte offsets of the tables below
+  uint64_t unit_offset;
+  uint64_t stream_offset;
+  uint64_t xcc_offset;
+  unsigned pad[44];
 };
 static_assert(sizeof(ChainHeader) == 256, "chain header is 256 bytes");
 
 struct ChainLinear {
-  const uint32_t* qweight;
-  const _Float16* scales;
-  const uint32_t* qzeros;
-  _Float16* out;         // fp16 [16][ldo] (NULL for the last linear)
-  float* partials;       // fp32 [splits][16][cb * wt * 64] when splits > 1
-  unsigned* tickets;     // [cb * wt] split arrivals per tile, one 256-byte slot each
-  unsigned* flags;       // [ceil(N / 64)] tile ready flags (epoch + 1 once written)
-  int K, N, ldo, splits;
-  int cb;                // column blocks of wt tiles
-  int units;             // cb * splits <= blocks: one unit per block
+  _Float16* out;         // fp16 [16][ld_out] (NULL for the last linear)
+  unsigned* flags;       // [tiles] output tile ready flags (epoch + 1 once written)
+  unsigned* sflags;      // [tiles][S] split partial ready flags (S > 1)
+  float* partials;       // per tile [S - 1][16][cols of the tile] fp32 (S > 1)
+  int K, N, ld_out;
   float alpha;
-  int wt;                // 64-column tiles per block (1, 2 or 4); 4 / wt k-slices
+  int S, tiles, pad0, pad1;
 };
-static_assert(sizeof(ChainLinear) == 88, "chain linear descriptor is 88 bytes");
+static_assert(sizeof(ChainLinear) == 64, "chain linear descriptor is 64 bytes");
 
-struct ChainLayout {
-  size_t bytes;          // total workspace bytes
-  size_t lin_offset;
-  size_t counters_offset;   // tickets and ready flags, zeroed by prepare
-  size_t buffers_offset;    // outputs and partials
+struct ChainUnit {       // block b's share of linear l
+  int col0;              // first output column (-1: no unit)
+  int nb;                // 16-column blocks
+  int g0, ng;            // 128-k groups
+  int split, S;          // K-split index and count of the unit's tile
+  int tile;              // tile index in the linear (flags, tickets, partials)
+  int f0, nf;            // input tiles of the previous linear this unit reads
+  unsigned soff;         // byte offset of the unit's data in the block's stream
+  int part_off;          // float offset of the tile's partials (S > 1)
+  unsigned gbytes;       // stream bytes per group (chain_group_bytes(nb))
 };
+static_assert(sizeof(ChainUnit) == 48, "chain unit descriptor is 48 bytes");
+
+struct ChainStream {     // block b's weight stream in the workspace
+  uint64_t offset;       // byte offset from the workspace start (1 KiB aligned)
+  unsigned kb;           // length in KiB
+  unsigned pad;
+};
+static_assert(sizeof(ChainStream) == 16, "chain stream descriptor is 16 bytes");
 
 hipError_t launch_w4a16_chain(ChainHeader* hdr, const _Float16* x, int64_t ldx, _Float16* y,
                               int64_t ldy, int M, int K0, int N_last, int blocks,
                               hipStream_t stream);
+// copies linear l's weights into the blocks' streams (grid: blocks x max groups per unit)
+hipError_t launch_w4a16_chain_prepack(const ChainUnit* units, const ChainStream* streams,
+                                      int blocks, int max_ng, const uint32_t* qweight,
+                                      const _Float16* scales, const uint32_t* qzeros, int N,
+                                      char* ws, hipStream_t stream);
 
 // ---------------------------------------------------------------- drafting
 constexpr int kNgramMaxN = 64;
