@@ -73,8 +73,7 @@ int w4v_abi_version(void);
  * Sizes    M >= 0 (M == 0 or N == 0: nothing to do, W4V_OK), K > 0,
  *          N % 8 == 0, K % group_size == 0; group_size must be 128 or 32,
  *          and K % 128 == 0 for both (W4V_ERR_UNSUPPORTED otherwise: the
- *          kernels step 128 k at a time).  On the in-register paths (M <= 32,
- *          and M >= 33 without a workspace) the packed weights (K*N/2 bytes),
+ *          kernels step 128 k at a time).  The packed weights (K*N/2 bytes),
  *          the scales and the rows of x (M*ldx*2 bytes) must each stay below
  *          2 GiB (W4V_ERR_UNSUPPORTED otherwise).
  * alpha    epilogue scale applied to the fp32 accumulator before the single
@@ -82,25 +81,24 @@ int w4v_abi_version(void);
  * Paths    M <= 32: weights dequantised exactly in registers, each group's
  *          scale applied to that group's fp32 sum (split-K across blocks).
  *          M >= 33 (the batched verify block, prefill shapes: bound by the
- *          matrix cores) with a workspace: the weights
- *          are first expanded to fp16 by this library's kernel,
- *          w = fp16_rne(float(s) * (q - z)) (one rounding; the fp32 product is
- *          exact), into the workspace, then multiplied by a plain fp16 GEMM of
- *          the vendor library (fp32 accumulation, same alpha and output
- *          rounding).  M >= 33 with no workspace at all (NULL and 0 bytes),
- *          or when the library offers no plan for the shape: the exact
- *          in-register arithmetic of M <= 32 in an LDS-tiled MFMA kernel.
+ *          matrix cores): an LDS-tiled MFMA kernel that dequantises each
+ *          256-column x 64-k weight tile once per 256-row block tile, as
+ *          w = fp16_rne(s * (q - z)) (q - z exact, one rounding; the fp32
+ *          accumulation and the alpha / output rounding as above); shapes with
+ *          few block tiles are split along K with fp32 partials in the
+ *          workspace, added in split order by a second kernel.  The plan (and
+ *          so the result) depends on the shape alone.
  * workspace  device memory of at least w4a16_gemm_workspace_size(M, N, K,
  *          group_size) bytes (may be NULL when that size is 0), 256-byte
  *          aligned, zeroed once by the caller.  Its first 64 KiB hold the
- *          split-K arrival counters (every call leaves them at zero), the next
- *          4 MiB at most the fp32 split-K partial sums (M <= 32); for M >= 33
- *          the fp16 expanded weights (2*K*N bytes) and the library GEMM's
- *          scratch come after those 4 MiB.  M >= 33 with a workspace smaller
- *          than the query's size (other than none at all): W4V_ERR_WORKSPACE.  The partials are added in split
- *          order, so the result does not depend on the order in which they
- *          arrive.  One workspace sized for the
- *          largest call serves calls of every shape ordered on one stream.
+ *          split-K arrival counters of the M <= 32 path (every call leaves them
+ *          at zero), the next 4 MiB at most that path's fp32 partial sums; the
+ *          M >= 33 path's fp32 partials [splits x M x N] come after those
+ *          4 MiB.  A workspace smaller than the query's size (NULL included)
+ *          returns W4V_ERR_WORKSPACE.  Partials are added in split order, so
+ *          the result does not depend on the order in which they arrive.  One
+ *          workspace sized for the largest call serves calls of every shape
+ *          ordered on one stream.
  * ---------------------------------------------------------------------- */
 size_t w4a16_gemm_workspace_size(int M, int N, int K, int group_size);
 

@@ -98,14 +98,18 @@ def test_gemm_workspace(lib):
     assert gemm(lib, K=4096, ldx=4096, g=32, ws=None, wsb=0) == WORKSPACE
     # sizes are a function of the shape alone
     assert w4v.gemm_workspace_size(16, 2560, 4096) == need
-    # from 33 rows on: the expanded fp16 weights and the library's scratch after the
-    # split-K regions; a partial workspace is an error, none at all selects the tiled kernel
+    # from 33 rows on: the LDS-tiled MFMA kernel; a plan with K-splits keeps its fp32
+    # partials [S][M][N] after the skinny kernel's regions and needs that workspace (none,
+    # or a smaller one, is an error), an unsplit plan needs none
     big = w4v.gemm_workspace_size(33, 2560, 4096)
-    assert big >= 2 * 2560 * 4096 + (64 << 10) + (4 << 20)
-    assert w4v.gemm_workspace_size(168, 2560, 4096) == big == w4v.gemm_workspace_size(8192, 2560, 4096)
+    rest = big - (64 << 10) - (4 << 20)
+    assert rest > 0 and rest % (33 * 2560 * 4) == 0 and rest // (33 * 2560 * 4) > 1
+    assert w4v.gemm_workspace_size(8192, 2560, 4096) == 0      # 320 block tiles: no split
+    assert w4v.gemm_workspace_size(33, 2560, 4096, 32) == big   # group size 32: same plan
     assert gemm(lib, M=33, K=4096, ldx=4096, ws=A * 256, wsb=big - 1) == WORKSPACE
-    assert gemm(lib, M=33, K=4096, ldx=4096, ws=A * 256, wsb=16) == WORKSPACE
-    # the tiled kernel keeps the 32-bit offset limits of the in-register paths
+    assert gemm(lib, M=33, K=4096, ldx=4096, ws=None, wsb=0) == WORKSPACE
+    assert gemm(lib, M=33, K=4096, ldx=4096, ws=A * 256 + 16, wsb=big) == ALIGN
+    # buffer resources take 32-bit offsets: weights of 2 GiB or more are refused
     assert gemm(lib, M=64, N=65536, K=65536, ldx=65536, ldy=65536, y=1 << 40,
                 ws=None, wsb=0) == UNSUPPORTED
 

@@ -29,7 +29,7 @@ def run_gemm(w4v, x, lin, alpha=1.0, ws=None, no_ws=False):
     (16, 9728, 2560),          # deep K (split across blocks)
     (16, 4096, 2560),
     (3, 9728, 1032),
-    (33, 256, 200),            # expansion + library GEMM from one row past a 32-row block
+    (33, 256, 200),            # the M >= 33 kernel from one row past a 32-row block
     (130, 384, 136),           # ragged rows and columns
     (300, 1280, 1032),
     (128, 128, 128),           # exactly one tile, one group
@@ -44,45 +44,49 @@ def test_random_shapes(lib, m, k, n):
     log(f"  rel-L2 {rel:.2e} max/rms {mx:.2e}")
 
 
-# ---- M >= 33 without a workspace: the LDS-tiled kernel (exact in-register dequantisation)
+# ---- M >= 33: the LDS-tiled MFMA kernel (weights dequantised per block tile into LDS as
+# fp16(s * (q - z)), split-K with fp32 partials in the workspace for shapes with few tiles)
 @pytest.mark.parametrize("m,k,n", [
     (33, 256, 200),            # one ragged row past a 32-row block
     (130, 384, 136),           # ragged rows and columns
     (300, 1280, 1032),
-    (128, 128, 128),           # exactly one tile, one group
+    (128, 128, 128),           # exactly one stage pair, one group
     (168, 2560, 2560),         # the padded verify batch of 8 x 21 rows
-    (600, 1280, 520),          # prefill-sized M on the tiled kernel
+    (600, 1280, 520),
+    (257, 4096, 264),          # one row and 8 columns past a 256 x 256 tile
 ])
-def test_tiled_kernel_without_workspace(lib, m, k, n):
-    log(f"gemm tiled m={m} k={k} n={n}")
+def test_mfma_kernel_shapes(lib, m, k, n):
+    log(f"gemm mfma m={m} k={k} n={n}")
     rng = np.random.default_rng(7000 + m * 7 + k + n)
     lin = gen.qlinear(rng, k, n)
     x = gen.activations(rng, m, k)
-    y = run_gemm(lib, x, lin, alpha=0.75, no_ws=True)
+    y = run_gemm(lib, x, lin, alpha=0.75)
     rel, mx = check_gemm(y, og.w4a16_gemm(x, lin.qweight, lin.scales, lin.qzeros, alpha=0.75),
-                         f"tiled {m}x{k}x{n}")
+                         f"mfma {m}x{k}x{n}")
     log(f"  rel-L2 {rel:.2e} max/rms {mx:.2e}")
 
 
-@pytest.mark.parametrize("enc", range(3))
-@pytest.mark.parametrize("m", [64, 200])
-def test_tiled_kernel_identity_bit_exact(lib, enc, m):
-    n = 512
-    eye = np.eye(n, dtype=np.int64)
-    g = n // 128
-    q, z, s = [
-        (eye, np.zeros((g, n), np.int64), np.ones((g, n), np.float16)),
-        (8 + eye, np.full((g, n), 8, np.int64), np.ones((g, n), np.float16)),
-        (7 + 2 * eye, np.full((g, n), 7, np.int64), np.full((g, n), 0.5, np.float16)),
-    ][enc]
-    lin = gen.QLinear(gen.pack_int4_along_k(q), s, gen.pack_int4_along_n(z), n, n)
-    x = gen.activations(np.random.default_rng(enc + 40), m, n)
-    y = run_gemm(lib, x, lin, no_ws=True)
-    assert np.array_equal(y.view(np.uint16), x.view(np.uint16))
+def test_mfma_split_plan_requires_its_workspace(lib):
+    """A shape whose plan splits K refuses to run without the workspace the query asks
+    for; a shape with one split needs none."""
+    import torch
+    rng = np.random.default_rng(77)
+    k, n, m = 9728, 2560, 168
+    assert lib.gemm_workspace_size(m, n, k) > 0
+    lin = gen.qlinear(rng, k, n)
+    x = gen.activations(rng, m, k)
+    with pytest.raises(lib.W4VError):
+        run_gemm(lib, x, lin, no_ws=True)
+    m2, k2, n2 = 4096, 256, 2048                 # 16 x 8 tiles over 4 stages: no split
+    assert lib.gemm_workspace_size(m2, n2, k2) == 0
+    lin2 = gen.qlinear(rng, k2, n2)
+    x2 = gen.activations(rng, m2, k2)
+    y2 = run_gemm(lib, x2, lin2, no_ws=True)
+    check_gemm(y2, og.w4a16_gemm(x2, lin2.qweight, lin2.scales, lin2.qzeros), "no split")
 
 
 @pytest.mark.parametrize("enc", range(3))
-@pytest.mark.parametrize("m", [16, 21, 64, 200])
+@pytest.mark.parametrize("m", [16, 21, 64, 200, 640])
 def test_identity_weights_bit_exact(lib, enc, m):
     n = 512
     eye = np.eye(n, dtype=np.int64)
@@ -186,33 +190,55 @@ def test_layer_linears_m16(lib, lin_idx):
     check_gemm(y, og.w4a16_gemm(x, lin.qweight, lin.scales, lin.qzeros, alpha=alpha), "layer")
 
 
-@pytest.mark.parametrize("m", [168, 2048, 8192])
+@pytest.mark.parametrize("shape", [(2560, 6144), (4096, 2560), (2560, 19456), (9728, 2560)])
+def test_padded_verify_block_full(lib, shape):
+    """The batched verify block (8 sequences x 21 rows): every output of every layer linear."""
+    k, n = shape
+    rng = np.random.default_rng(168 + k + n)
+    lin = gen.qlinear(rng, k, n)
+    x = gen.activations(rng, 168, k)
+    a = gen.chain_alpha(k)
+    y = run_gemm(lib, x, lin, alpha=a)
+    rel, mx = check_gemm(y, og.w4a16_gemm(x, lin.qweight, lin.scales, lin.qzeros, alpha=a),
+                         f"m=168 {k}->{n}")
+    log(f"  m=168 {k}->{n}: rel-L2 {rel:.2e} max/rms {mx:.2e}")
+
+
+@pytest.mark.parametrize("m", [2048, 8192])
 @pytest.mark.parametrize("shape", [(2560, 19456), (9728, 2560)])
-def test_large_m_sampled_columns(lib, m, shape):
-    """Verify-batch (M = 168) and prefill (M = 2048, 8192) shapes: every row, sampled columns."""
+def test_prefill_rows_and_columns(lib, m, shape):
+    """Prefill shapes (M = 2048, 8192): the fp64 oracle of the whole product is 0.1-0.8
+    TFLOP, minutes on the host, so every output row is checked on 64 columns and 96 rows
+    (including the first and last, and rows of every 256-row tile) on every column; every
+    block tile of the output is covered."""
     k, n = shape
     wl = gen.make_workload(5, m=m)
     lin = wl.linears[0] if k == 2560 else wl.linears[1]
     x = wl.extra_x[0] if k == 2560 else wl.extra_x[1]
-    log(f"large-m m={m} {k}->{n}")
+    log(f"prefill m={m} {k}->{n}")
     y = run_gemm(lib, x, lin)
+    assert np.all(np.isfinite(y.astype(np.float32)))
     rng = np.random.default_rng(m + k)
-    cols = np.sort(rng.choice(n, 96, replace=False))
+    cols = np.sort(rng.choice(n, 64, replace=False))
     cols[0], cols[-1] = 0, n - 1
     ref = og.w4a16_gemm_columns(x, lin.qweight, lin.scales, lin.qzeros, cols)
-    check_gemm(y[:, cols], ref, f"m={m} {k}->{n}")
-    assert np.all(np.isfinite(y.astype(np.float32)))
+    rel, _ = check_gemm(y[:, cols], ref, f"m={m} {k}->{n} all rows")
+    tiles = np.arange(0, m, 256)
+    rows = np.unique(np.concatenate([[0, m - 1], tiles + rng.integers(0, 256, tiles.size),
+                                     rng.choice(m, 96 - tiles.size - 2, replace=False)]))
+    ref_r = og.w4a16_gemm(x[rows], lin.qweight, lin.scales, lin.qzeros)
+    rel_r, _ = check_gemm(y[rows], ref_r, f"m={m} {k}->{n} all columns")
+    log(f"  rel-L2 {rel:.2e} (all rows) {rel_r:.2e} ({rows.size} rows, all columns)")
 
 
-# ---- M >= 33 with a workspace: weights dequantised to fp16 by the library's kernel, then a
-# plain fp16 GEMM
+# ---- M >= 33 path, more shapes (the split and unsplit plans)
 @pytest.mark.parametrize("m,k,n", [
     (511, 384, 136),
     (512, 384, 136),           # ragged N
     (600, 1280, 1032),
     (1000, 128, 8),            # one group, narrowest N
 ])
-def test_library_path_shapes(lib, m, k, n):
+def test_mfma_path_shapes(lib, m, k, n):
     log(f"gemm m={m} k={k} n={n}")
     rng = np.random.default_rng(3000 + m + k + n)
     lin = gen.qlinear(rng, k, n)
@@ -223,26 +249,9 @@ def test_library_path_shapes(lib, m, k, n):
     log(f"  rel-L2 {rel:.2e} max/rms {mx:.2e}")
 
 
-@pytest.mark.parametrize("enc", range(3))
-def test_library_path_identity_bit_exact(lib, enc):
-    """Identity weights stay exact through the fp16 expansion (q - z in {0, 1}, scale 1 or 0.5 x 2)."""
-    n, m = 512, 640
-    eye = np.eye(n, dtype=np.int64)
-    g = n // 128
-    q, z, s = [
-        (eye, np.zeros((g, n), np.int64), np.ones((g, n), np.float16)),
-        (8 + eye, np.full((g, n), 8, np.int64), np.ones((g, n), np.float16)),
-        (7 + 2 * eye, np.full((g, n), 7, np.int64), np.full((g, n), 0.5, np.float16)),
-    ][enc]
-    lin = gen.QLinear(gen.pack_int4_along_k(q), s, gen.pack_int4_along_n(z), n, n)
-    x = gen.activations(np.random.default_rng(enc), m, n)
-    y = run_gemm(lib, x, lin)
-    assert np.array_equal(y.view(np.uint16), x.view(np.uint16))
-
-
-def test_library_path_strided_and_shared_workspace(lib):
+def test_mfma_path_strided_and_shared_workspace(lib):
     """Row-strided x and y at M = 700, then M = 16 split-K calls on the same workspace: the
-    counter prefix the split-K path relies on is left at zero by the expanded-weight path."""
+    counter prefix the skinny split-K path relies on is left at zero by the M >= 33 path."""
     import torch
     rng = np.random.default_rng(31)
     k, n, m = 1024, 520, 700

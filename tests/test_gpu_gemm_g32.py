@@ -1,6 +1,6 @@
 """GPU parity of the W4A16 linear at group size 32 (results page, section 5:
-team #5's compressed-tensors target) against the fp64 oracle on all three
-paths (M <= 32 skinny; M >= 33 expansion + library GEMM, or LDS-tiled without a workspace),
+team #5's compressed-tensors target) against the fp64 oracle on both paths
+(M <= 32 skinny; M >= 33 the LDS-tiled MFMA kernel, split or unsplit),
 exact identity and one-hot cases whose scale and zero-point change every 32 k,
 and the 4B-class layer's linears at M = 16."""
 import numpy as np
@@ -28,15 +28,13 @@ def run_gemm(w4v, x, lin, alpha=1.0, ws=None, no_ws=False):
     (21, 1280, 520),           # K = 20 verify block: two m-tiles
     (16, 9728, 2560),          # deep K: split across blocks
     (5, 128, 8),               # one 128-k step, four groups, narrowest N
-    (33, 256, 200),            # expansion + library GEMM, ragged rows and columns
+    (33, 256, 200),            # the M >= 33 kernel, ragged rows and columns
     (200, 1280, 1032),
     (512, 384, 136),
     (640, 1280, 1032),
 ])
-@pytest.mark.parametrize("no_ws", [False, True])
-def test_random_shapes_group_32(lib, m, k, n, no_ws):
-    if no_ws and m <= 32:
-        pytest.skip("the in-register split-K path needs its workspace")
+def test_random_shapes_group_32(lib, m, k, n):
+    no_ws = lib.gemm_workspace_size(m, n, k, GS) == 0
     log(f"gemm g32 m={m} k={k} n={n} no_ws={no_ws}")
     rng = np.random.default_rng(5000 + m + k + n)
     lin = gen.qlinear(rng, k, n, group_size=GS)
@@ -48,11 +46,9 @@ def test_random_shapes_group_32(lib, m, k, n, no_ws):
 
 
 @pytest.mark.parametrize("enc", range(3))
-@pytest.mark.parametrize("m,no_ws", [(16, False), (21, False), (64, False), (640, False),
-                                     (64, True), (200, True)])
-def test_identity_weights_bit_exact_group_32(lib, enc, m, no_ws):
-    """q - z in {0, 1} (or {0, 2} at scale 0.5) with the zero-point changing every 32 k
-    (no_ws: the LDS-tiled kernel)."""
+@pytest.mark.parametrize("m", [16, 21, 64, 200, 640])
+def test_identity_weights_bit_exact_group_32(lib, enc, m):
+    """q - z in {0, 1} (or {0, 2} at scale 0.5) with the zero-point changing every 32 k."""
     n = 512
     g = n // GS
     eye = np.eye(n, dtype=np.int64)
@@ -65,12 +61,12 @@ def test_identity_weights_bit_exact_group_32(lib, enc, m, no_ws):
     ][enc]
     lin = gen.QLinear(gen.pack_int4_along_k(q), s, gen.pack_int4_along_n(z), n, n, GS)
     x = gen.activations(np.random.default_rng(enc + m), m, n)
-    y = run_gemm(lib, x, lin, no_ws=no_ws)
+    y = run_gemm(lib, x, lin)
     assert np.array_equal(y.view(np.uint16), x.view(np.uint16))
 
 
-@pytest.mark.parametrize("m,no_ws", [(16, False), (64, False), (64, True)])
-def test_one_hot_weight_with_per_group_scales(lib, m, no_ws):
+@pytest.mark.parametrize("m", [16, 64, 300])
+def test_one_hot_weight_with_per_group_scales(lib, m):
     """A single nonzero weight in the third 32-k group of a 128-k step; every group has
     its own scale and zero-point, so a group index off by one changes the result."""
     k, n = 512, 264
@@ -83,7 +79,7 @@ def test_one_hot_weight_with_per_group_scales(lib, m, no_ws):
     z = np.repeat(zg[:, None], n, 1)
     lin = gen.QLinear(gen.pack_int4_along_k(q), s.astype(np.float16), gen.pack_int4_along_n(z), k, n, GS)
     x = gen.activations(np.random.default_rng(9 + m), m, k)
-    y = run_gemm(lib, x, lin, no_ws=no_ws)
+    y = run_gemm(lib, x, lin)
     w = float(s[k0 // GS, n0]) * float(q[k0, n0] - zg[k0 // GS])
     expect = np.zeros((m, n), dtype=np.float16)
     expect[:, n0] = (x[:, k0].astype(np.float64) * w).astype(np.float16)

@@ -157,8 +157,8 @@ def w4a16_gemm(x, qweight, scales, qzeros, alpha: float = 1.0, out=None, workspa
     x: fp16 [M, >=K] (a column slice of a wider tensor is fine: its row stride
     is passed as ldx); qweight: int32 [K/8, N]; scales: fp16 [K/g, N];
     qzeros: int32 [K/g, N/8] with g = group_size (128 or 32).  ``out`` may be a
-    row-strided fp16 [M, N] view.  ``no_workspace`` passes none at all (for
-    M >= 33 the library then runs its LDS-tiled kernel).
+    row-strided fp16 [M, N] view.  ``no_workspace`` passes none at all (a shape
+    whose plan needs a workspace then fails with W4V_ERR_WORKSPACE).
     """
     torch = _require(x, __import__("torch").float16, "x")
     _require(qweight, torch.int32, "qweight")

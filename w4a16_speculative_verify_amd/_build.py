@@ -13,9 +13,9 @@ INCLUDE = os.path.join(ROOT, "include")
 OBJDIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libw4v.so")
 
-SOURCES = ["w4a16_skinny.hip", "w4a16_tiled.hip", "w4a16_dequant.hip", "w4a16_chain.hip",
+SOURCES = ["w4a16_skinny.hip", "w4a16_mfma.hip", "w4a16_chain.hip",
            "w8a16_lmhead.hip", "greedy_verify.hip", "ngram_draft.hip", "gdn_commit.hip", "lib_gemm.cpp", "api.cpp"]
-# the vendor GEMM library behind the prefill-shaped linear's plain fp16 product
+# the vendor GEMM library behind the fp16 linear (f16_gemm) only
 LIBS = ["-L/opt/rocm/lib", "-lhipblaslt", "-Wl,-rpath,/opt/rocm/lib"]
 
 # gfx950 only.  Packed-fp32 instructions are switched off for every HIP

@@ -303,21 +303,20 @@ const char* w4v_status_string(int status) {
 
 int w4v_abi_version(void) { return W4V_ABI_VERSION; }
 
-// Workspace of the library path (M >= kLibMinRows): the counter prefix and
-// the split-K partials region are left alone (so one workspace still serves
-// calls of every shape), then the transposed fp16 weights, then the library
-// GEMM's scratch.
+// Offset of everything after the split-K counter prefix and the skinny
+// kernel's partials region: the fp32 partials of the M >= 33 path and the
+// fp16 linear's library scratch start here, so one workspace serves calls of
+// every shape ordered on one stream.
 static size_t lib_offset() { return w4v::kTicketRegion + w4v::kPartialRegion; }
-static size_t lib_weights_bytes(int N, int K) { return w4v::align_up((size_t)N * K * 2, 256); }
-static size_t lib_workspace_bytes(int N, int K) {
-  return lib_offset() + lib_weights_bytes(N, K) + w4v::kLibWorkspace;
-}
 
 size_t w4a16_gemm_workspace_size(int M, int N, int K, int group_size) {
   if (M <= 0 || N <= 0 || K <= 0 || (group_size != w4v::kGroup && group_size != 32) ||
       K % w4v::kGroup != 0 || N % 8 != 0)
     return 0;
-  if (M >= w4v::kLibMinRows) return lib_workspace_bytes(N, K);
+  if (M >= w4v::kMfmaMinRows) {
+    const w4v::MfmaPlan p = w4v::plan_w4a16_mfma(M, N, K, kPlanCUs);
+    return p.splits > 1 ? lib_offset() + p.partial_bytes : 0;
+  }
   return w4v::plan_w4a16(M, N, K, kPlanCUs).workspace_bytes();
 }
 
@@ -326,29 +325,10 @@ int w4a16_gemm(const void* x, int64_t ldx, const int32_t* qweight, const void* s
                float alpha, void* workspace, size_t workspace_bytes, void* stream) {
   int st = gemm_check(x, ldx, qweight, scales, qzeros, y, ldy, M, N, K, group_size);
   if (st != W4V_OK || M == 0 || N == 0) return st;
-  // 33 rows and more: the library path with a workspace, the LDS-tiled
-  // kernel (no workspace needed) when none is given at all
-  const bool many = M >= w4v::kTiledMinRows;
-  const bool lib = many && M >= w4v::kLibMinRows && !(workspace == nullptr && workspace_bytes == 0);
-  const bool tiled = many;
-  if (tiled && (M + 127) / 128 > kMaxGridYZ) return W4V_ERR_UNSUPPORTED;
   // buffer resources take 32-bit offsets below 2 GiB
-  const bool big = (size_t)K * N / 2 >= (1ull << 31) || (size_t)M * ldx * 2 >= (1ull << 31) ||
-                   (size_t)(K / group_size) * N * 2 >= (1ull << 31);
-  if (tiled && !lib && big) return W4V_ERR_UNSUPPORTED;
-  if (lib) {
-    st = workspace_check(lib_workspace_bytes(N, K), workspace, workspace_bytes);
-    if (st != W4V_OK) return st;
-  }
-  w4v::GemmPlan p{};
-  if (!tiled) {
-    p = w4v::plan_w4a16(M, N, K, kPlanCUs);
-    if (big || p.mblocks > kMaxGridYZ || p.splits > kMaxGridYZ ||
-        p.partial_bytes > w4v::kPartialRegion)
-      return W4V_ERR_UNSUPPORTED;
-    st = workspace_check(p.workspace_bytes(), workspace, workspace_bytes);
-    if (st != W4V_OK) return st;
-  }
+  if ((size_t)K * N / 2 >= (1ull << 31) || (size_t)M * ldx * 2 >= (1ull << 31) ||
+      (size_t)(K / group_size) * N * 2 >= (1ull << 31))
+    return W4V_ERR_UNSUPPORTED;
   w4v::GemmArgs a{};
   a.x = static_cast<const _Float16*>(x);
   a.ldx = ldx;
@@ -363,21 +343,26 @@ int w4a16_gemm(const void* x, int64_t ldx, const int32_t* qweight, const void* s
   a.alpha = alpha;
   a.group_size = group_size;
   const hipStream_t s = static_cast<hipStream_t>(stream);
-  if (lib) {
-    // weights to fp16 (our kernel), then the plain GEMM; if the library has
-    // no plan for the shape (or the weights exceed the tiled kernel's range
-    // anyway), the LDS-tiled kernel computes the same product
-    char* base = static_cast<char*>(workspace) + lib_offset();
-    _Float16* wt = reinterpret_cast<_Float16*>(base);
-    hipError_t e = w4v::launch_dequant_w4_f16t(a.qweight, a.scales, a.qzeros, K, N, group_size,
-                                               wt, s);
-    if (e != hipSuccess) return W4V_ERR_HIP;
-    if (w4v::lib_gemm_f16_tn(a.x, ldx, wt, K, a.y, ldy, M, N, K, alpha,
-                             base + lib_weights_bytes(N, K), w4v::kLibWorkspace, s))
-      return W4V_OK;
-    if (big) return W4V_ERR_HIP;
+  if (M >= w4v::kMfmaMinRows) {
+    // one path for every call of this shape: the plan depends on the shape
+    // alone, and a plan with K-splits requires its workspace
+    const w4v::MfmaPlan p = w4v::plan_w4a16_mfma(M, N, K, kPlanCUs);
+    if (p.mblocks * p.nblocks > INT32_MAX / 64 || p.splits > kMaxGridYZ) return W4V_ERR_UNSUPPORTED;
+    float* partials = nullptr;
+    if (p.splits > 1) {
+      st = workspace_check(lib_offset() + p.partial_bytes, workspace, workspace_bytes);
+      if (st != W4V_OK) return st;
+      partials = reinterpret_cast<float*>(static_cast<char*>(workspace) + lib_offset());
+    }
+    hipError_t e = w4v::launch_w4a16_mfma(a, p, partials, s);
+    return e == hipSuccess ? W4V_OK : W4V_ERR_HIP;
   }
-  hipError_t e = tiled ? w4v::launch_w4a16_tiled(a, s) : w4v::launch_w4a16_skinny(a, p, workspace, s);
+  const w4v::GemmPlan p = w4v::plan_w4a16(M, N, K, kPlanCUs);
+  if (p.mblocks > kMaxGridYZ || p.splits > kMaxGridYZ || p.partial_bytes > w4v::kPartialRegion)
+    return W4V_ERR_UNSUPPORTED;
+  st = workspace_check(p.workspace_bytes(), workspace, workspace_bytes);
+  if (st != W4V_OK) return st;
+  hipError_t e = w4v::launch_w4a16_skinny(a, p, workspace, s);
   return e == hipSuccess ? W4V_OK : W4V_ERR_HIP;
 }
 

@@ -55,21 +55,24 @@ struct GemmPlan {
 GemmPlan plan_w4a16(int M, int N, int K, int num_cus);
 hipError_t launch_w4a16_skinny(const GemmArgs& a, const GemmPlan& p, void* workspace,
                                hipStream_t stream);
-// LDS-tiled MFMA GEMM for M > 32 rows (no workspace)
-hipError_t launch_w4a16_tiled(const GemmArgs& a, hipStream_t stream);
-constexpr int kTiledMinRows = 33;
 
-// From this many rows on, with a workspace: weights dequantised to a
-// transposed fp16 copy in the workspace, then a plain fp16 GEMM from the
-// vendor library (without a workspace: the LDS-tiled kernel).
-constexpr int kLibMinRows = 33;
+// From this many rows on: the LDS-tiled MFMA kernel (weights dequantised once
+// per 256 x 256 block tile into LDS), split-K with fp32 partials in the
+// workspace for shapes with few tiles
+constexpr int kMfmaMinRows = 33;
+struct MfmaPlan {
+  int mblocks, nblocks;  // 256 x 256 block tiles
+  int splits;            // K-splits (1 = none)
+  size_t partial_bytes;  // fp32 [splits][M][N] when splits > 1
+};
+MfmaPlan plan_w4a16_mfma(int M, int N, int K, int num_cus);
+hipError_t launch_w4a16_mfma(const GemmArgs& a, const MfmaPlan& p, float* partials,
+                             hipStream_t stream);
+
+// y = alpha * x @ wt^T through the vendor library (wt: fp16 [N x K], row
+// stride ldw); false if the library has no plan for the shape or reports an
+// error before launching (the fp16 linear only)
 constexpr size_t kLibWorkspace = 64ull << 20;   // the library GEMM's own scratch
-hipError_t launch_dequant_w4_f16t(const uint32_t* qweight, const _Float16* scales,
-                                  const uint32_t* qzeros, int K, int N, int group_size,
-                                  _Float16* wt, hipStream_t stream);
-// y = alpha * x @ wt^T through the library (wt: fp16 [N x K], row stride
-// ldw); false if the library has no plan for the shape or reports an error
-// before launching.
 bool lib_gemm_f16_tn(const _Float16* x, int64_t ldx, const _Float16* wt, int64_t ldw, _Float16* y,
                      int64_t ldy, int M, int N, int K, float alpha, void* scratch,
                      size_t scratch_bytes, hipStream_t stream);
