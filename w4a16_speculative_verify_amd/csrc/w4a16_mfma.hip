@@ -4,24 +4,39 @@
 // bucket's cost is prefill compute), so the 4-bit weights are dequantised
 // once per block tile into LDS and shared by all of the tile's rows.
 //
-// Block tile 256 rows x 256 columns, 64 k per stage, two LDS stages:
-//   A  the activations, copied global -> LDS by LDS DMA (buffer_load_dwordx4
-//      ... lds, no registers), 16-byte chunks of 8 k placed at
-//      slot = row * 8 + (chunk ^ (row % 8)) so that the MFMA A reads of 8
-//      consecutive rows fall in different banks;
-//   B  the packed words of the stage (8 packed rows x 256 columns), loaded
-//      into registers, dequantised in natural k order to
-//      fp16(s * (q - z)) -- q - z exact, one rounding for the scale, the
-//      fp32 accumulation unchanged -- and stored as 8 k per 16-byte chunk at
-//      slot = n * 8 + (chunk ^ ((n / 4) % 8)).
-// 8 waves as 2 (rows) x 4 (columns), each 128 x 64: 8 x 4 v_mfma_f32_16x16x32_f16
-// tiles with fp32 accumulators.  MFMA column j of the wave's column tile c is
-// output column 4 j + c, so every lane ends up with 4 adjacent columns of each
-// row it holds and stores them as one 8-byte write.  While a stage's MFMAs
-// run, the next stage's A is in flight to the other LDS buffer and its packed
-// words to registers; they are dequantised into LDS after the MFMAs.
+// Block tile 256 rows x 256 columns, 32 k per stage.  Every global load is an
+// LDS DMA (buffer_load ... lds: no registers; issued from inline assembly so
+// that the compiler does not wait for it at unrelated LDS accesses -- the
+// kernel waits itself with explicit vmcnt counts), kSlots stages deep in a
+// ring of LDS slots, so that a stage's data has three stages of MFMA time to
+// arrive.  A slot holds one stage's
+//   A     256 rows x 32 k fp16, row r's 16-byte chunk c stored at
+//         r * 4 + (c ^ sw(r));
+//   W     the packed words, 4 packed rows x 256 columns;
+//   meta  the stage's quantisation group: 256 fp16 scales, 32 zero words.
+// One stage ahead of the MFMAs, the block dequantises the next stage's words
+// from LDS into a double-buffered fp16 B tile in natural k order, as
+// fp16(s * (q - z)) (q - z exact, one rounding for the scale, the fp32
+// accumulation unchanged).  Column 64 g + 4 j + c of the tile sits at
+// position v = 64 g + 16 c + j, its chunk c' at v * 4 + (c' ^ sw(v)).
+// LDS on gfx950 (measured): 64 banks of 4 bytes; a 16-byte read serves in
+// one cycle the 4 lane quads of a 32-lane half whose quad index (lane bits
+// 2..4) has the same bit parity, a 16-byte write 8 consecutive lanes.  For an
+// MFMA operand read (16 rows, 4 k-chunks over the wave) that means rows
+// {0-3, 12-15} of one chunk with rows {4-11} of the next in one cycle;
+// sw(i) = -(i / 4) mod 4 spreads each such set over all 64 banks, and keeps
+// the 8 consecutive positions of a dequantisation write in distinct banks.
+// 8 waves as 2 (rows) x 4 (columns) of 128 x 64: 8 x 4 v_mfma_f32_16x16x32_f16
+// tiles with fp32 accumulators; MFMA tile c of a wave reads positions
+// 16 c .. 16 c + 15 of its 64, i.e. columns 4 j + c, so every lane ends up with
+// 4 adjacent columns of each row it holds and stores them with one write.
+// One block barrier per stage; after it the next stage's words are
+// dequantised and the stage kSlots - 1 ahead is requested, then the MFMAs run.
 // Blocks are ordered in groups of 8 row blocks, so that the blocks running
 // together share their activation rows and packed weights in L2.
+// Split-K: block (tile, split) computes a contiguous range of stages; with
+// S > 1 it stores fp32 partials [split][M][N] and a second kernel adds them in
+// split order.
 #include "w4v_device.h"
 #include "w4v_launch.h"
 
@@ -29,21 +44,28 @@ namespace w4v {
 
 namespace {
 
-constexpr int BM = 256, BN = 256, BK = 64;
+constexpr int BM = 256, BN = 256, BK = 32;
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kGroupM = 8;                          // row blocks per raster group
-constexpr int kAStage = BM * BK * 2;                // 32 KiB
-constexpr int kBStage = BN * BK * 2;                // 32 KiB
+constexpr int kSlots = 5;                           // stages resident in LDS
+constexpr int kAhead = kSlots - 1;                  // stages requested ahead of the MFMAs
+constexpr uint32_t kA = 0, kW = 16384, kScale = 20480, kZero = 21504;   // offsets in a slot
+constexpr uint32_t kSlotBytes = 22528;
+constexpr uint32_t kBTile = 16384;                  // fp16 B tile: 256 columns x 32 k
+constexpr uint32_t kSink = kSlots * kSlotBytes + 2 * kBTile;   // 1 KiB for DMAs with no data
+constexpr uint32_t kLdsBytes = kSink + 1024;
+constexpr uint32_t kNoMem = 0x80000000u;            // past every resource: reads no memory
+
+__device__ __forceinline__ int sw(int i) { return (4 - ((i >> 2) & 3)) & 3; }
 
 typedef uint32_t u32x4s __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ u32x4s dma_rsrc(const void* base, uint32_t bytes) {
+__device__ __forceinline__ u32x4s dma_rsrc(const void* base) {
   const uint64_t a = reinterpret_cast<uint64_t>(base);
-  return u32x4s{(uint32_t)a, (uint32_t)(a >> 32) & 0xffffu, bytes, 0x00020000u};
+  return u32x4s{(uint32_t)a, (uint32_t)(a >> 32) & 0xffffu, 0x7fffffffu, 0x00020000u};
 }
-// 16 bytes per lane global -> LDS at M0 + 16 * lane (M0 saved and restored);
-// from inline assembly so that the compiler does not wait for these copies
-// before every LDS access of the other stage (the kernel waits itself)
+// global -> LDS, 16 (dma16) or 4 (dma4) bytes per lane to M0 + size * lane
+// (M0 saved and restored); every wave issues three per stage
 __device__ __forceinline__ void dma16(uint32_t lds_addr, u32x4s src, uint32_t off) {
   uint32_t saved;
   asm volatile(
@@ -53,7 +75,15 @@ __device__ __forceinline__ void dma16(uint32_t lds_addr, u32x4s src, uint32_t of
       : "s"(lds_addr), "v"(off), "s"(src)
       : "memory");
 }
-
+__device__ __forceinline__ void dma4(uint32_t lds_addr, u32x4s src, uint32_t off) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\t"
+      "buffer_load_dword %2, %3, 0 offen lds\n\ts_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds_addr), "v"(off), "s"(src)
+      : "memory");
+}
 // packed word (8 consecutive k of one column) -> 8 fp16 s * (q - z) in natural
 // k order: bytes of w and w >> 4 interleaved by v_perm so that pair p holds
 // nibbles 2p and 2p + 1, each OR-ed under 1024.0 (exact 1024 + q), then
@@ -70,13 +100,10 @@ __device__ __forceinline__ u32x4 dequant_natural(uint32_t w, f16x2 z1024, f16x2 
   return u32x4{f(p0), f(p1), f(p2), f(p3)};
 }
 
-// Split-K: block (tile, split) computes stages [stages * split / S, stages *
-// (split + 1) / S); with S > 1 it stores fp32 partials [split][M][N] and a
-// second kernel adds them in split order.
 template <int Q>    // 1: group size 128, 4: group size 32
 __global__ __launch_bounds__(kThreads) void w4a16_mfma_kernel(GemmArgs a, int mblocks, int nblocks,
                                                               int S, float* partials) {
-  __shared__ __attribute__((aligned(16))) unsigned char lds[2 * (kAStage + kBStage)];
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[kLdsBytes];
   const int t = threadIdx.x;
   const int lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
@@ -92,66 +119,108 @@ __global__ __launch_bounds__(kThreads) void w4a16_mfma_kernel(GemmArgs a, int mb
   const int mblk = m_first + (bid % per_group) % gm;
   const int nblk = (bid % per_group) / gm;
   const int m0 = mblk * BM, n0 = nblk * BN;
-  const int M = a.M, N = a.N, K = a.K;
+  const int M = a.M, N = a.N;
   const int split = blockIdx.y;
-  const int s_lo = (K / BK) * split / S, s_hi = (K / BK) * (split + 1) / S;
+  const int stages = a.K / BK;
+  const int s_lo = stages * split / S, s_hi = stages * (split + 1) / S;
 
-  const uint32_t lds_base = (uint32_t)reinterpret_cast<uintptr_t>(
+  const uint32_t lds0 = (uint32_t)reinterpret_cast<uintptr_t>(
       (__attribute__((address_space(3))) unsigned char*)lds);
-  auto a_lds = [&](int s) { return lds_base + (uint32_t)(s & 1) * (kAStage + kBStage); };
-  auto a_ptr = [&](int s) { return lds + (s & 1) * (kAStage + kBStage); };
-  auto b_ptr = [&](int s) { return a_ptr(s) + kAStage; };
 
-  // ---- A copy: wave w moves rows 32 w .. 32 w + 31 (4 instructions of 8 rows)
-  //      lane l of instruction i: LDS slot 64 i + l = row 8 i + l / 8, stored
-  //      chunk l % 8 holding logical chunk (l % 8) ^ (row % 8)
-  const u32x4s rx = dma_rsrc(a.x, 0x7fffffffu);
-  uint32_t a_off[4];
+  // ---- the wave's three DMAs of a stage (offsets for stage 0):
+  //   two of 16 activation rows (rows 32 wave + 16 i + lane / 4, stored chunk
+  //   lane % 4); then waves 0-3 packed row `wave` of the stage's four, wave 4
+  //   the scales, wave 5 the zero words, waves 6 and 7 nothing (into the sink)
+  const u32x4s rx = dma_rsrc(a.x);
+  uint32_t xo[2];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = wave * 32 + i * 8 + (lane >> 3);
+  for (int i = 0; i < 2; ++i) {
+    const int r = wave * 32 + i * 16 + (lane >> 2);
     const int m = m0 + r < M ? m0 + r : M - 1;      // rows past M: read a valid row, never stored
-    const int chunk = (lane & 7) ^ (r & 7);
-    a_off[i] = ((uint32_t)m * (uint32_t)a.ldx + (uint32_t)chunk * 8) * 2;
+    const int chunk = (lane & 3) ^ sw(r);
+    xo[i] = ((uint32_t)m * (uint32_t)a.ldx + (uint32_t)chunk * 8) * 2;
   }
-  auto copy_a = [&](int s) {
-    const uint32_t base = a_lds(s) + (uint32_t)wave * 32 * 128;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) dma16(base + i * 1024, rx, a_off[i] + (uint32_t)s * BK * 2);
+  const uint32_t Nu = (uint32_t)N;
+  u32x4s r3 = dma_rsrc(a.qweight);
+  uint32_t o3 = kNoMem, d3 = kSink;                 // third DMA: source offset, LDS offset
+  uint32_t step3 = 0;                               // its source step per stage (waves 0-3)
+  if (wave < 4) {
+    const uint32_t c = (uint32_t)(n0 + 4 * lane);
+    o3 = c < Nu ? ((uint32_t)wave * Nu + c) * 4 : kNoMem;
+    d3 = kW + (uint32_t)wave * 1024;
+    step3 = 4 * Nu * 4;
+  } else if (wave == 4) {
+    r3 = dma_rsrc(a.scales);
+    const uint32_t c = (uint32_t)(n0 + 8 * lane);
+    o3 = lane < 32 && c < Nu ? c * 2 : kNoMem;
+    d3 = kScale;
+  } else if (wave == 5) {
+    r3 = dma_rsrc(a.qzeros);
+    const uint32_t c = (uint32_t)(n0 + 8 * lane);
+    o3 = lane < 32 && c < Nu ? (c >> 3) * 4 : kNoMem;
+    d3 = kZero;
+  }
+  const uint32_t gstep = wave == 4 ? Nu * 2 : (Nu >> 3) * 4;     // meta bytes per group
+  // stage s into its slot; a stage past the block's range is requested too,
+  // with no source (kNoMem: zeros into a free slot), so that every stage costs
+  // a wave exactly three DMAs and the waits below are fixed counts
+  auto issue = [&](int s) {
+    const bool live = s < s_hi;
+    const uint32_t slot = lds0 + (uint32_t)((s - s_lo) % kSlots) * kSlotBytes;
+    const uint32_t base = slot + kA + (uint32_t)wave * 2048;
+    dma16(base, rx, live ? xo[0] + (uint32_t)s * BK * 2 : kNoMem);
+    dma16(base + 1024, rx, live ? xo[1] + (uint32_t)s * BK * 2 : kNoMem);
+    uint32_t o = o3;
+    if (o != kNoMem)
+      o += wave < 4 ? (uint32_t)s * step3 : (uint32_t)(s * BK / (128 / Q)) * gstep;
+    o = live ? o : kNoMem;
+    const uint32_t d = d3 == kSink ? lds0 + kSink : slot + d3;
+    if (wave == 5) dma4(d, r3, o);
+    else dma16(d, r3, o);
   };
 
-  // ---- B: thread t dequantises column n_t, chunks 4 h .. 4 h + 3 (32 k) of a
-  //      stage, h = t / 256; lanes 8 j .. 8 j + 7 take columns whose n / 4
-  //      differ, so that their LDS stores fall in different banks
-  const int h = t >> 8;
-  const int tn = t & 255;
-  const int ncol = (tn & ~31) + ((tn & 7) << 2) + ((tn >> 3) & 3);
-  const int gcol_raw = n0 + ncol;
-  const bool col_ok = gcol_raw < N;
-  const int gcol = col_ok ? gcol_raw : N - 1;
-  const rsrc_t rw = make_rsrc(a.qweight), rs = make_rsrc(a.scales), rz = make_rsrc(a.qzeros);
-  const uint32_t Nu = (uint32_t)N;
-  auto load_b = [&](int s, uint32_t (&w)[4], uint32_t& zw, uint32_t& sv) {
-    const uint32_t prow = (uint32_t)(s * BK / 8 + h * 4);         // first packed row
-#pragma unroll
-    for (int j = 0; j < 4; ++j) w[j] = ld_x1(rw, ((prow + j) * Nu + (uint32_t)gcol) * 4);
-    const uint32_t g = (uint32_t)((s * BK + h * 32) / (128 / Q));  // quantisation group
-    zw = ld_x1(rz, (g * (Nu >> 3) + ((uint32_t)gcol >> 3)) * 4);
-    sv = ld_x1(rs, (g * Nu + (uint32_t)gcol) * 2 & ~3u);          // the dword holding the scale
-  };
+  // ---- dequantisation: thread t fills B-tile position v = t % 256 (column
+  //      dn), chunks 2 (t / 256) and 2 (t / 256) + 1.  Split in its LDS reads
+  //      and its arithmetic + writes, so that the arithmetic can run between
+  //      the MFMAs of the stage before.
+  const int v = t & 255, dh = t >> 8;
+  const int dn = (v & ~63) | ((v & 15) << 2) | ((v >> 4) & 3);
   const uint32_t magic = in_vgpr(0x64006400u);
-  auto store_b = [&](int s, const uint32_t (&w)[4], uint32_t zw, uint32_t sv) {
-    const uint32_t z = (zw >> (4 * (gcol & 7))) & 0xFu;
+  struct DqIn { uint32_t zw, sb, w0, w1; };
+  auto dq_read = [&](int s) {
+    const unsigned char* slot = lds + ((s - s_lo) % kSlots) * kSlotBytes;
+    DqIn d;
+    d.zw = *reinterpret_cast<const uint32_t*>(slot + kZero + (dn >> 3) * 4);
+    d.sb = *reinterpret_cast<const unsigned short*>(slot + kScale + dn * 2);
+    d.w0 = *reinterpret_cast<const uint32_t*>(slot + kW + ((dh * 2) * 256 + dn) * 4);
+    d.w1 = *reinterpret_cast<const uint32_t*>(slot + kW + ((dh * 2 + 1) * 256 + dn) * 4);
+    return d;
+  };
+  const int bw0 = (v * 4 + ((dh * 2) ^ sw(v))) * 16, bw1 = (v * 4 + ((dh * 2 + 1) ^ sw(v))) * 16;
+  auto dq_write = [&](int s, const DqIn& d) {
+    const uint32_t z = (d.zw >> (4 * (dn & 7))) & 0xFu;
     const f16x2 z1024 = __builtin_bit_cast(f16x2, (0x6400u | z) * 0x00010001u);
-    const uint32_t sbits = (gcol & 1) ? (sv >> 16) : (sv & 0xffffu);
-    const f16x2 sc = __builtin_bit_cast(f16x2, sbits * 0x00010001u);
-    unsigned char* bp = b_ptr(s);
+    const f16x2 sc = __builtin_bit_cast(f16x2, d.sb * 0x00010001u);
+    unsigned char* bt = lds + kSlots * kSlotBytes + ((s - s_lo) & 1) * kBTile;
+    *reinterpret_cast<u32x4*>(bt + bw0) = dequant_natural(d.w0, z1024, sc, magic);
+    *reinterpret_cast<u32x4*>(bt + bw1) = dequant_natural(d.w1, z1024, sc, magic);
+  };
+
+  int ao[8], bo[4];                                 // MFMA operand offsets within a tile
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int chunk = h * 4 + j;
-      const int slot = ncol * 8 + (chunk ^ ((ncol >> 2) & 7));
-      *reinterpret_cast<u32x4*>(bp + slot * 16) = dequant_natural(w[j], z1024, sc, magic);
-    }
+  for (int mt = 0; mt < 8; ++mt) {
+    const int r = wm * 128 + mt * 16 + l16;
+    ao[mt] = (r * 4 + (kb ^ sw(r))) * 16;
+  }
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const int p = wn * 64 + c * 16 + l16;
+    bo[c] = (p * 4 + (kb ^ sw(p))) * 16;
+  }
+  auto read_a = [&](int s, f16x8 (&av)[8]) {
+    const unsigned char* as = lds + ((s - s_lo) % kSlots) * kSlotBytes + kA;
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt) av[mt] = *reinterpret_cast<const f16x8*>(as + ao[mt]);
   };
 
   f32x4 acc[8][4];
@@ -160,46 +229,53 @@ __global__ __launch_bounds__(kThreads) void w4a16_mfma_kernel(GemmArgs a, int mb
 #pragma unroll
     for (int c = 0; c < 4; ++c) acc[i][c] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // ---- prologue: the first stage in LDS
-  uint32_t wr[4], zw, sv;
-  copy_a(s_lo);
-  load_b(s_lo, wr, zw, sv);
-  store_b(s_lo, wr, zw, sv);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
+  // ---- one stage: B fragments of stage s, the next stage's words and A
+  //      fragments read, stage s + kAhead requested, then the 32 MFMAs with the
+  //      next stage's dequantisation between them.  On entry stage s + 1 has
+  //      landed for this wave (DMAs of the two stages after it may still be in
+  //      flight); after the barrier it has for every wave, B(s) is complete and
+  //      every wave is done with the slot and B tile of stage s - 1.
+  auto step = [&](int s, const f16x8 (&av)[8], f16x8 (&an)[8]) {
+    __builtin_amdgcn_s_waitcnt(0x0f76);             // vmcnt(6): two stages still in flight
+    lds_barrier();
+    const unsigned char* bs = lds + kSlots * kSlotBytes + ((s - s_lo) & 1) * kBTile;
+    f16x8 bv[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) bv[c] = *reinterpret_cast<const f16x8*>(bs + bo[c]);
+    const DqIn d = dq_read(s + 1);
+    read_a(s + 1, an);
+    issue(s + kAhead);
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) acc[mt][c] = mfma16x16x32(av[mt], bv[c], acc[mt][c]);
+    dq_write(s + 1, d);
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);      // B fragment reads
+    __builtin_amdgcn_sched_group_barrier(0x100, 12, 0);     // dequant inputs, next A fragments
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);    // one MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);    // two VALU
+    }
+    __builtin_amdgcn_sched_group_barrier(0x200, 2, 0);      // B tile writes
+  };
 
-  // MFMA A rows of this wave: 128 wm + 16 mt + l16; B columns: 64 wn + 4 j + c
-  for (int s = s_lo; s < s_hi; ++s) {
-    const bool more = s + 1 < s_hi;
-    if (more) {
-      copy_a(s + 1);
-      load_b(s + 1, wr, zw, sv);
-    }
-    const unsigned char* ap = a_ptr(s);
-    const unsigned char* bp = b_ptr(s);
+  // ---- prologue: request the first kAhead stages, dequantise the first
+  //      stage and read its A fragments
 #pragma unroll
-    for (int it = 0; it < 2; ++it) {                // two 32-k slabs
-      const int chunk = it * 4 + kb;
-      f16x8 av[8], bv[4];
-#pragma unroll
-      for (int mt = 0; mt < 8; ++mt) {
-        const int r = wm * 128 + mt * 16 + l16;
-        av[mt] = *reinterpret_cast<const f16x8*>(ap + (r * 8 + (chunk ^ (r & 7))) * 16);
-      }
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const int n = wn * 64 + 4 * l16 + c;
-        bv[c] = *reinterpret_cast<const f16x8*>(bp + (n * 8 + (chunk ^ ((n >> 2) & 7))) * 16);
-      }
-#pragma unroll
-      for (int mt = 0; mt < 8; ++mt)
-#pragma unroll
-        for (int c = 0; c < 4; ++c) acc[mt][c] = mfma16x16x32(av[mt], bv[c], acc[mt][c]);
-    }
-    if (more) store_b(s + 1, wr, zw, sv);
-    __builtin_amdgcn_s_waitcnt(0);                  // the next stage's A copies have landed
-    __syncthreads();
+  for (int i = 0; i < kAhead; ++i) issue(s_lo + i);
+  __builtin_amdgcn_s_waitcnt(0x0f79);               // vmcnt(9): stage s_lo has landed
+  lds_barrier();
+  dq_write(s_lo, dq_read(s_lo));
+  f16x8 a0[8], a1[8];
+  read_a(s_lo, a0);
+
+  int s = s_lo;
+  for (; s + 1 < s_hi; s += 2) {
+    step(s, a0, a1);
+    step(s + 1, a1, a0);
   }
+  if (s < s_hi) step(s, a0, a1);
 
   // ---- epilogue: lane holds rows 16 mt + 4 kb + e, columns 4 l16 .. + 3 of its tile
   const int col = n0 + wn * 64 + 4 * l16;
@@ -212,8 +288,8 @@ __global__ __launch_bounds__(kThreads) void w4a16_mfma_kernel(GemmArgs a, int mb
       for (int e = 0; e < 4; ++e) {
         const int m = m0 + wm * 128 + mt * 16 + 4 * kb + e;
         if (m < M) {
-          const f32x4 v = {acc[mt][0][e], acc[mt][1][e], acc[mt][2][e], acc[mt][3][e]};
-          *reinterpret_cast<f32x4*>(pp + (size_t)m * N + col) = v;
+          const f32x4 val = {acc[mt][0][e], acc[mt][1][e], acc[mt][2][e], acc[mt][3][e]};
+          *reinterpret_cast<f32x4*>(pp + (size_t)m * N + col) = val;
         }
       }
     return;
@@ -226,8 +302,8 @@ __global__ __launch_bounds__(kThreads) void w4a16_mfma_kernel(GemmArgs a, int mb
       if (m < M) {
         const f16x2 lo = {(_Float16)(a.alpha * acc[mt][0][e]), (_Float16)(a.alpha * acc[mt][1][e])};
         const f16x2 hi = {(_Float16)(a.alpha * acc[mt][2][e]), (_Float16)(a.alpha * acc[mt][3][e])};
-        const u32x2 v = {__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
-        *reinterpret_cast<u32x2*>(a.y + (size_t)m * a.ldy + col) = v;
+        const u32x2 val = {__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
+        *reinterpret_cast<u32x2*>(a.y + (size_t)m * a.ldy + col) = val;
       }
     }
 }
@@ -257,14 +333,14 @@ MfmaPlan plan_w4a16_mfma(int M, int N, int K, int num_cus) {
   p.nblocks = (N + BN - 1) / BN;
   const int tiles = p.mblocks * p.nblocks;
   const int stages = K / BK;
-  // time ~ rounds of blocks (one block per CU) x stages per block, plus for
-  // S > 1 the partials written and read again (2 S M N fp32 at ~5 TB/s, in
-  // stage units of ~1 us) and the reduce launch
+  // time ~ rounds of blocks (one block per CU) x stages per block (~0.5 us
+  // each), plus for S > 1 the partials written and read again (2 S M N fp32
+  // at ~5 TB/s) and the reduce launch
   double best = 0;
   p.splits = 1;
-  for (int S = 1; S <= 32 && stages / S >= 4; ++S) {
+  for (int S = 1; S <= 32 && stages / S >= 8; ++S) {
     const double rounds = (double)((tiles * S + num_cus - 1) / num_cus);
-    double t = rounds * ((stages + S - 1) / S);
+    double t = rounds * ((stages + S - 1) / S) * 0.5;
     if (S > 1) t += 2.0 * S * M * (double)N * 4 / 5e6 + 3.0;
     if (S == 1 || t < best - 1e-9) {
       best = t;
