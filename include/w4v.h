@@ -109,6 +109,29 @@ int w4a16_gemm(const void* x, int64_t ldx,
                void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * W4A16 linear that allocates nothing, for callers that cannot allocate
+ * device memory or pass a workspace: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc.
+ *
+ * Same arguments, results (bit for bit) and launch plan as w4a16_gemm, minus
+ * the workspace: the scratch a plan needs lives in a device array of
+ * W4V_STATIC_SCRATCH_BYTES that the library holds on every GPU it runs on
+ * until the process ends.  A shape whose w4a16_gemm_workspace_size exceeds
+ * that returns W4V_ERR_UNSUPPORTED before any launch.  The first calls on a
+ * device clear the array's ticket region with a small kernel on `stream`
+ * (also when captured); the kernels re-arm it after every call.
+ * Calls on one GPU share the array: two calls whose executions overlap on
+ * one GPU (different streams, or graphs replayed concurrently) race, so
+ * order them on one stream.  Never calls hipMalloc or hipFree.
+ * ---------------------------------------------------------------------- */
+#define W4V_STATIC_SCRATCH_BYTES (32u << 20)
+
+int w4a16_gemm_noalloc(const void* x, int64_t ldx,
+                       const int32_t* qweight, const void* scales, const int32_t* qzeros,
+                       void* y, int64_t ldy,
+                       int M, int N, int K, int group_size, float alpha, void* stream);
+
+/* ------------------------------------------------------------------------
  * 8-bit lm_head with fused greedy argmax (section 3: untied lm_head
  * quantised to 8 bits, temperature-0 serving; section 5: W8A16 lm_head)
  *

@@ -114,6 +114,35 @@ def test_gemm_workspace(lib):
                 ws=None, wsb=0) == UNSUPPORTED
 
 
+def gemm_na(lib, x=A, ldx=2560, qw=A, sc=A, qz=A, y=A * 64, ldy=2560, M=16, N=2560, K=2560, g=128):
+    return lib.w4a16_gemm_noalloc(x, ldx, qw, sc, qz, y, ldy, M, N, K, g, ctypes.c_float(1.0), None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(g=64), UNSUPPORTED),
+    (dict(K=100, ldx=128), INVALID),
+    (dict(x=None), INVALID),
+    (dict(ldy=2000), INVALID),
+    (dict(x=A + 2), ALIGN),
+    (dict(y=A + 256), INVALID),                   # y overlaps x
+    (dict(M=0), OK),
+    # the plan's workspace would not fit the static scratch (43.5 MB > 32 MiB)
+    (dict(M=168, N=19456, ldy=19456, y=1 << 40), UNSUPPORTED),
+    (dict(M=8192, K=9728, ldx=9728, y=1 << 40), UNSUPPORTED),
+])
+def test_gemm_noalloc_validation(lib, kw, status):
+    assert gemm_na(lib, **kw) == status
+
+
+def test_static_scratch_limit(lib):
+    assert w4v.STATIC_SCRATCH_BYTES == 32 << 20
+    # every skinny plan (M <= 32) fits: 64 KiB of tickets + at most 4 MiB of partials
+    for m, k, n in ((16, 9728, 2560), (32, 4096, 2560), (1, 2560, 19456)):
+        assert w4v.gemm_workspace_size(m, n, k) <= w4v.STATIC_SCRATCH_BYTES
+    assert w4v.gemm_workspace_size(168, 6144, 2560) <= w4v.STATIC_SCRATCH_BYTES
+    assert w4v.gemm_workspace_size(168, 19456, 2560) > w4v.STATIC_SCRATCH_BYTES
+
+
 def lm(lib, h=A, ldh=2560, w=A, sc=A, t=A, ml=None, M=16, H=2560, V=4096, ws=A * 256, wsb=1 << 30):
     return lib.w8a16_lmhead_argmax(h, ldh, w, sc, t, ml, M, H, V, ws, wsb, None)
 

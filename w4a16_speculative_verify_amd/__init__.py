@@ -40,6 +40,8 @@ SIGNATURES = {
     "w4a16_gemm_workspace_size": (_sz, [_int, _int, _int, _int]),
     "w4a16_gemm": (_int, [_vp, _i64, _vp, _vp, _vp, _vp, _i64, _int, _int, _int, _int,
                           ctypes.c_float, _vp, _sz, _vp]),
+    "w4a16_gemm_noalloc": (_int, [_vp, _i64, _vp, _vp, _vp, _vp, _i64, _int, _int, _int, _int,
+                                  ctypes.c_float, _vp]),
     "w8a16_lmhead_argmax_workspace_size": (_sz, [_int, _int, _int]),
     "w8a16_lmhead_argmax": (_int, [_vp, _i64, _vp, _vp, _vp, _vp, _int, _int, _int, _vp, _sz,
                                    _vp]),
@@ -186,6 +188,34 @@ def w4a16_gemm(x, qweight, scales, qzeros, alpha: float = 1.0, out=None, workspa
                            _ptr(out), out.stride(0), m, n, k, group_size, ctypes.c_float(alpha),
                            _ptr(workspace), wbytes, _stream(stream))
     _check(st, "w4a16_gemm")
+    return out
+
+
+STATIC_SCRATCH_BYTES = 32 << 20     # W4V_STATIC_SCRATCH_BYTES
+
+
+def w4a16_gemm_noalloc(x, qweight, scales, qzeros, alpha: float = 1.0, out=None,
+                       group_size: int = GROUP_SIZE, stream=None):
+    """w4a16_gemm without a workspace: the library's per-GPU static scratch
+    holds the plan's split-K state.  ``out`` must be given when the caller
+    cannot allocate (otherwise one fp16 [M, N] tensor is allocated here).
+    Shapes needing more than STATIC_SCRATCH_BYTES raise W4VError."""
+    torch = _require(x, __import__("torch").float16, "x")
+    _require(qweight, torch.int32, "qweight")
+    _require(scales, torch.float16, "scales")
+    _require(qzeros, torch.int32, "qzeros")
+    k = qweight.shape[0] * 8
+    n = qweight.shape[1]
+    m = x.shape[0]
+    if x.shape[1] < k:
+        raise ValueError(f"x has {x.shape[1]} columns, the weights need {k}")
+    if out is None:
+        out = torch.empty((m, n), dtype=torch.float16, device=x.device)
+    _require(out, torch.float16, "out")
+    st = load().w4a16_gemm_noalloc(_ptr(x), x.stride(0), _ptr(qweight), _ptr(scales),
+                                   _ptr(qzeros), _ptr(out), out.stride(0), m, n, k, group_size,
+                                   ctypes.c_float(alpha), _stream(stream))
+    _check(st, "w4a16_gemm_noalloc")
     return out
 
 

@@ -7,6 +7,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 #include <vector>
 
 #include "w4v.h"
@@ -287,6 +288,55 @@ int chain_blocks() {
 
 }  // namespace
 
+// ------------------------------------------------------------ static scratch
+// Device memory of w4a16_gemm_noalloc: the layout of a w4a16_gemm workspace
+// (split-K tickets, the skinny path's partials, the M >= 33 path's partials)
+// in a file-scope device array.  Every GPU the library runs on holds its own
+// copy from the time the library's code is loaded on it until the process
+// ends.  Host code never uses the array's name as an address: each device's
+// address comes from hipGetSymbolAddress (scratch_for_current_device).
+static __device__ __attribute__((aligned(256))) unsigned char scratch[W4V_STATIC_SCRATCH_BYTES];
+
+__global__ void w4v_zero_words(unsigned* p, unsigned n) {
+  for (unsigned i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = 0u;
+}
+
+namespace {
+
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxScratchDevices];     // per device: the array's device address
+bool g_scratch_clear[kMaxScratchDevices];    // per device: tickets cleared by an eager call
+
+// The scratch array's address on the current device.  Until a call that is
+// not under stream capture has cleared the ticket region (with a fill kernel
+// on the caller's stream, ordered before the GEMM), every call clears it, so
+// that a graph captured before that carries its own clear.
+int scratch_for_current_device(hipStream_t stream, void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return W4V_ERR_HIP;
+  if (dev < 0 || dev >= kMaxScratchDevices) return W4V_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return W4V_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  if (!g_scratch_clear[dev]) {
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(stream, &cap) != hipSuccess) return W4V_ERR_HIP;
+    const unsigned words = (unsigned)(w4v::kTicketRegion / sizeof(unsigned));
+    hipLaunchKernelGGL(w4v_zero_words, dim3((words + 255) / 256), dim3(256), 0, stream,
+                       static_cast<unsigned*>(g_scratch_ptr[dev]), words);
+    if (hipGetLastError() != hipSuccess) return W4V_ERR_HIP;
+    if (cap == hipStreamCaptureStatusNone) g_scratch_clear[dev] = true;
+  }
+  *out = g_scratch_ptr[dev];
+  return W4V_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 const char* w4v_status_string(int status) {
@@ -364,6 +414,22 @@ int w4a16_gemm(const void* x, int64_t ldx, const int32_t* qweight, const void* s
   if (st != W4V_OK) return st;
   hipError_t e = w4v::launch_w4a16_skinny(a, p, workspace, s);
   return e == hipSuccess ? W4V_OK : W4V_ERR_HIP;
+}
+
+int w4a16_gemm_noalloc(const void* x, int64_t ldx, const int32_t* qweight, const void* scales,
+                       const int32_t* qzeros, void* y, int64_t ldy, int M, int N, int K,
+                       int group_size, float alpha, void* stream) {
+  int st = gemm_check(x, ldx, qweight, scales, qzeros, y, ldy, M, N, K, group_size);
+  if (st != W4V_OK || M == 0 || N == 0) return st;
+  const size_t need = w4a16_gemm_workspace_size(M, N, K, group_size);
+  if (need > W4V_STATIC_SCRATCH_BYTES) return W4V_ERR_UNSUPPORTED;
+  void* ws = nullptr;
+  if (need > 0) {
+    st = scratch_for_current_device(static_cast<hipStream_t>(stream), &ws);
+    if (st != W4V_OK) return st;
+  }
+  return w4a16_gemm(x, ldx, qweight, scales, qzeros, y, ldy, M, N, K, group_size, alpha, ws,
+                    ws ? (size_t)W4V_STATIC_SCRATCH_BYTES : 0, stream);
 }
 
 size_t w8a16_lmhead_argmax_workspace_size(int M, int H, int V) {
