@@ -206,29 +206,18 @@ def test_padded_verify_block_full(lib, shape):
 
 @pytest.mark.parametrize("m", [2048, 8192])
 @pytest.mark.parametrize("shape", [(2560, 19456), (9728, 2560)])
-def test_prefill_rows_and_columns(lib, m, shape):
-    """Prefill shapes (M = 2048, 8192): the fp64 oracle of the whole product is 0.1-0.8
-    TFLOP, minutes on the host, so every output row is checked on 64 columns and 96 rows
-    (including the first and last, and rows of every 256-row tile) on every column; every
-    block tile of the output is covered."""
+def test_prefill_full_output(lib, m, shape):
+    """Prefill shapes (M = 2048, 8192): every output element against the fp64 oracle of
+    the whole product (0.1-0.8 TFLOP of fp64, seconds on the host)."""
     k, n = shape
     wl = gen.make_workload(5, m=m)
     lin = wl.linears[0] if k == 2560 else wl.linears[1]
     x = wl.extra_x[0] if k == 2560 else wl.extra_x[1]
     log(f"prefill m={m} {k}->{n}")
     y = run_gemm(lib, x, lin)
-    assert np.all(np.isfinite(y.astype(np.float32)))
-    rng = np.random.default_rng(m + k)
-    cols = np.sort(rng.choice(n, 64, replace=False))
-    cols[0], cols[-1] = 0, n - 1
-    ref = og.w4a16_gemm_columns(x, lin.qweight, lin.scales, lin.qzeros, cols)
-    rel, _ = check_gemm(y[:, cols], ref, f"m={m} {k}->{n} all rows")
-    tiles = np.arange(0, m, 256)
-    rows = np.unique(np.concatenate([[0, m - 1], tiles + rng.integers(0, 256, tiles.size),
-                                     rng.choice(m, 96 - tiles.size - 2, replace=False)]))
-    ref_r = og.w4a16_gemm(x[rows], lin.qweight, lin.scales, lin.qzeros)
-    rel_r, _ = check_gemm(y[rows], ref_r, f"m={m} {k}->{n} all columns")
-    log(f"  rel-L2 {rel:.2e} (all rows) {rel_r:.2e} ({rows.size} rows, all columns)")
+    ref = og.w4a16_gemm(x, lin.qweight, lin.scales, lin.qzeros)
+    rel, mx = check_gemm(y, ref, f"m={m} {k}->{n}")
+    log(f"  rel-L2 {rel:.2e} max/rms {mx:.2e} over all {m} x {n} outputs")
 
 
 # ---- M >= 33 path, more shapes (the split and unsplit plans)

@@ -63,9 +63,10 @@ def test_ties_go_to_lowest_index(lib, m):
         assert t[i] == min(cands[i])
 
 
-def test_int8_extremes(lib):
-    rng = np.random.default_rng(6)
-    v, m = 3000, 16
+@pytest.mark.parametrize("m", [16, 168])
+def test_int8_extremes(lib, m):
+    rng = np.random.default_rng(6 + m)
+    v = 3000
     w8 = rng.choice(np.array([-128, -127, 127], dtype=np.int8), size=(v, gen.HIDDEN))
     s8 = gen.lmhead_scales(rng, v)
     h = gen.activations(rng, m, gen.HIDDEN)
@@ -73,14 +74,15 @@ def test_int8_extremes(lib):
     check_argmax(t, olm.logits(h, w8, s8), "extremes")
 
 
-def test_one_hot_hidden(lib):
-    rng = np.random.default_rng(8)
-    v, m = 5000, 16
+@pytest.mark.parametrize("m", [16, 168])
+def test_one_hot_hidden(lib, m):
+    rng = np.random.default_rng(8 + m)
+    v = 5000
     w8 = gen.lmhead_weights(rng, v, gen.HIDDEN)
     s8 = gen.lmhead_scales(rng, v)
     h = np.zeros((m, gen.HIDDEN), dtype=np.float16)
     for i in range(m):
-        h[i, 160 * i + 3] = 1.0
+        h[i, (157 * i + 3) % gen.HIDDEN] = 1.0
     t, mx = run_lm(lib, h, w8, s8)
     lg = olm.logits(h, w8, s8)
     t_o, top, _ = olm.argmax_margin(lg)

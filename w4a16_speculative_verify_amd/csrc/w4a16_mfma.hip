@@ -11,27 +11,22 @@
 // ring of LDS slots, so that a stage's data has three stages of MFMA time to
 // arrive.  A slot holds one stage's
 //   A     256 rows x 32 k fp16, row r's 16-byte chunk c stored at
-//         r * 4 + (c ^ sw(r));
+//         r * 4 + (c ^ lds_sw4(r));
 //   W     the packed words, 4 packed rows x 256 columns;
 //   meta  the stage's quantisation group: 256 fp16 scales, 32 zero words.
 // One stage ahead of the MFMAs, the block dequantises the next stage's words
 // from LDS into a double-buffered fp16 B tile in natural k order, as
 // fp16(s * (q - z)) (q - z exact, one rounding for the scale, the fp32
 // accumulation unchanged).  Column 64 g + 4 j + c of the tile sits at
-// position v = 64 g + 16 c + j, its chunk c' at v * 4 + (c' ^ sw(v)).
-// LDS on gfx950 (measured): 64 banks of 4 bytes; a 16-byte read serves in
-// one cycle the 4 lane quads of a 32-lane half whose quad index (lane bits
-// 2..4) has the same bit parity, a 16-byte write 8 consecutive lanes.  For an
-// MFMA operand read (16 rows, 4 k-chunks over the wave) that means rows
-// {0-3, 12-15} of one chunk with rows {4-11} of the next in one cycle;
-// sw(i) = -(i / 4) mod 4 spreads each such set over all 64 banks, and keeps
-// the 8 consecutive positions of a dequantisation write in distinct banks.
+// position v = 64 g + 16 c + j, its chunk c' at v * 4 + (c' ^ lds_sw4(v)).
+// The row swizzle lds_sw4 (w4v_device.h) keeps the MFMA operand reads and
+// the dequantisation writes free of LDS bank conflicts.
 // 8 waves as 2 (rows) x 4 (columns) of 128 x 64: 8 x 4 v_mfma_f32_16x16x32_f16
 // tiles with fp32 accumulators; MFMA tile c of a wave reads positions
 // 16 c .. 16 c + 15 of its 64, i.e. columns 4 j + c, so every lane ends up with
 // 4 adjacent columns of each row it holds and stores them with one write.
-// One block barrier per stage; after it the next stage's words are
-// dequantised and the stage kSlots - 1 ahead is requested, then the MFMAs run.
+// One block barrier per stage; after it the MFMAs run with the next stage's
+// dequantisation between them, then the stage kSlots - 1 ahead is requested.
 // Blocks are ordered in groups of 8 row blocks, so that the blocks running
 // together share their activation rows and packed weights in L2.
 // Split-K: block (tile, split) computes a contiguous range of stages; with
@@ -57,33 +52,6 @@ constexpr uint32_t kSink = kSlots * kSlotBytes + 2 * kBTile;   // 1 KiB for DMAs
 constexpr uint32_t kLdsBytes = kSink + 1024;
 constexpr uint32_t kNoMem = 0x80000000u;            // past every resource: reads no memory
 
-__device__ __forceinline__ int sw(int i) { return (4 - ((i >> 2) & 3)) & 3; }
-
-typedef uint32_t u32x4s __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ u32x4s dma_rsrc(const void* base) {
-  const uint64_t a = reinterpret_cast<uint64_t>(base);
-  return u32x4s{(uint32_t)a, (uint32_t)(a >> 32) & 0xffffu, 0x7fffffffu, 0x00020000u};
-}
-// global -> LDS, 16 (dma16) or 4 (dma4) bytes per lane to M0 + size * lane
-// (M0 saved and restored); every wave issues three per stage
-__device__ __forceinline__ void dma16(uint32_t lds_addr, u32x4s src, uint32_t off) {
-  uint32_t saved;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\t"
-      "buffer_load_dwordx4 %2, %3, 0 offen lds\n\ts_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "s"(lds_addr), "v"(off), "s"(src)
-      : "memory");
-}
-__device__ __forceinline__ void dma4(uint32_t lds_addr, u32x4s src, uint32_t off) {
-  uint32_t saved;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\t"
-      "buffer_load_dword %2, %3, 0 offen lds\n\ts_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "s"(lds_addr), "v"(off), "s"(src)
-      : "memory");
-}
 // packed word (8 consecutive k of one column) -> 8 fp16 s * (q - z) in natural
 // k order: bytes of w and w >> 4 interleaved by v_perm so that pair p holds
 // nibbles 2p and 2p + 1, each OR-ed under 1024.0 (exact 1024 + q), then
@@ -137,7 +105,7 @@ __global__ __launch_bounds__(kThreads) void w4a16_mfma_kernel(GemmArgs a, int mb
   for (int i = 0; i < 2; ++i) {
     const int r = wave * 32 + i * 16 + (lane >> 2);
     const int m = m0 + r < M ? m0 + r : M - 1;      // rows past M: read a valid row, never stored
-    const int chunk = (lane & 3) ^ sw(r);
+    const int chunk = (lane & 3) ^ lds_sw4(r);
     xo[i] = ((uint32_t)m * (uint32_t)a.ldx + (uint32_t)chunk * 8) * 2;
   }
   const uint32_t Nu = (uint32_t)N;
@@ -196,7 +164,7 @@ __global__ __launch_bounds__(kThreads) void w4a16_mfma_kernel(GemmArgs a, int mb
     d.w1 = *reinterpret_cast<const uint32_t*>(slot + kW + ((dh * 2 + 1) * 256 + dn) * 4);
     return d;
   };
-  const int bw0 = (v * 4 + ((dh * 2) ^ sw(v))) * 16, bw1 = (v * 4 + ((dh * 2 + 1) ^ sw(v))) * 16;
+  const int bw0 = (v * 4 + ((dh * 2) ^ lds_sw4(v))) * 16, bw1 = (v * 4 + ((dh * 2 + 1) ^ lds_sw4(v))) * 16;
   auto dq_write = [&](int s, const DqIn& d) {
     const uint32_t z = (d.zw >> (4 * (dn & 7))) & 0xFu;
     const f16x2 z1024 = __builtin_bit_cast(f16x2, (0x6400u | z) * 0x00010001u);
@@ -210,12 +178,12 @@ __global__ __launch_bounds__(kThreads) void w4a16_mfma_kernel(GemmArgs a, int mb
 #pragma unroll
   for (int mt = 0; mt < 8; ++mt) {
     const int r = wm * 128 + mt * 16 + l16;
-    ao[mt] = (r * 4 + (kb ^ sw(r))) * 16;
+    ao[mt] = (r * 4 + (kb ^ lds_sw4(r))) * 16;
   }
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
     const int p = wn * 64 + c * 16 + l16;
-    bo[c] = (p * 4 + (kb ^ sw(p))) * 16;
+    bo[c] = (p * 4 + (kb ^ lds_sw4(p))) * 16;
   }
   auto read_a = [&](int s, f16x8 (&av)[8]) {
     const unsigned char* as = lds + ((s - s_lo) % kSlots) * kSlotBytes + kA;
@@ -230,8 +198,8 @@ __global__ __launch_bounds__(kThreads) void w4a16_mfma_kernel(GemmArgs a, int mb
     for (int c = 0; c < 4; ++c) acc[i][c] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // ---- one stage: B fragments of stage s, the next stage's words and A
-  //      fragments read, stage s + kAhead requested, then the 32 MFMAs with the
-  //      next stage's dequantisation between them.  On entry stage s + 1 has
+  //      fragments read, the 32 MFMAs with the next stage's dequantisation
+  //      between them, then stage s + kAhead requested.  On entry stage s + 1 has
   //      landed for this wave (DMAs of the two stages after it may still be in
   //      flight); after the barrier it has for every wave, B(s) is complete and
   //      every wave is done with the slot and B tile of stage s - 1.
@@ -244,12 +212,15 @@ __global__ __launch_bounds__(kThreads) void w4a16_mfma_kernel(GemmArgs a, int mb
     for (int c = 0; c < 4; ++c) bv[c] = *reinterpret_cast<const f16x8*>(bs + bo[c]);
     const DqIn d = dq_read(s + 1);
     read_a(s + 1, an);
-    issue(s + kAhead);
 #pragma unroll
     for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
       for (int c = 0; c < 4; ++c) acc[mt][c] = mfma16x16x32(av[mt], bv[c], acc[mt][c]);
     dq_write(s + 1, d);
+    // last: a DMA instruction can stall its wave at issue while the memory
+    // path is busy; issued after the MFMAs, the stall of one wave leaves the
+    // matrix unit to the other wave of its SIMD
+    issue(s + kAhead);
     __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);      // B fragment reads
     __builtin_amdgcn_sched_group_barrier(0x100, 12, 0);     // dequant inputs, next A fragments
 #pragma unroll

@@ -207,6 +207,44 @@ __device__ __forceinline__ bool arrive_last(unsigned* ticket, unsigned count) {
   return last;
 }
 
+// ---- global -> LDS copies without registers (buffer_load ... lds) ----------
+// Lane l's 16 bytes land at M0 + 16 l.  Issued from inline assembly so that
+// the compiler does not wait for them at unrelated LDS accesses; the kernels
+// that use them wait with explicit vmcnt counts (M0 saved and restored).
+typedef uint32_t u32x4s __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ u32x4s dma_rsrc(const void* base) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  return u32x4s{(uint32_t)a, (uint32_t)(a >> 32) & 0xffffu, 0x7fffffffu, 0x00020000u};
+}
+__device__ __forceinline__ void dma16(uint32_t lds_addr, u32x4s src, uint32_t off) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\t"
+      "buffer_load_dwordx4 %2, %3, 0 offen lds\n\ts_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds_addr), "v"(off), "s"(src)
+      : "memory");
+}
+// The same with 4 bytes per lane (to M0 + 4 l).
+__device__ __forceinline__ void dma4(uint32_t lds_addr, u32x4s src, uint32_t off) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\t"
+      "buffer_load_dword %2, %3, 0 offen lds\n\ts_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds_addr), "v"(off), "s"(src)
+      : "memory");
+}
+// LDS row swizzle for tiles of 64-byte rows (four 16-byte chunks): chunk c of
+// row r sits at r * 4 + (c ^ lds_sw4(r)).  gfx950 LDS (measured): 64 banks of
+// 4 bytes; a 16-byte read serves in one cycle the 4 lane quads of a 32-lane
+// half whose quad index (lane bits 2..4) has the same bit parity, a 16-byte
+// write 8 consecutive lanes.  For an MFMA operand read (16 consecutive rows,
+// chunk l / 16) that is rows {0-3, 12-15} of one chunk with rows {4-11} of
+// the next; -(r / 4) mod 4 spreads each such set over all 64 banks and keeps
+// 8 consecutive rows of one chunk in distinct banks for the writes.
+__device__ __forceinline__ int lds_sw4(int r) { return (4 - ((r >> 2) & 3)) & 3; }
+
 // Total order for greedy argmax: larger value first, then lower index.
 __device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
   return v > bv || (v == bv && i < bi);
