@@ -53,27 +53,60 @@ def lmhead_bytes(m, h, v, k_draft):
 
 def cpu_baseline(wl, plan, drafts, min_seconds: float = 10.0):
     """Time the oracle on whole verify steps of the same workload (36 layers at
-    M = 16, the full lm_head, greedy verify) until ``min_seconds`` have passed."""
+    M = 16, the full lm_head, greedy verify) until ``min_seconds`` have passed,
+    with numpy's BLAS on every core the process may use (``cores`` reports the
+    BLAS threads actually in use, ``affinity_cores`` the cores available); plus
+    the small block-linear step (one 2560 -> 2560 linear, a 4096-word head,
+    greedy verify) on one thread."""
     import numpy as np
+    from threadpoolctl import threadpool_info, threadpool_limits
     from oracle import step as ostep
 
-    cores = min(len(os.sched_getaffinity(0)), 16)
-    steps = 0
-    t0 = time.perf_counter()
-    while True:
-        ostep.verify_step(wl.x, wl.linears, plan, wl.lm_w, wl.lm_s, drafts, 1, drafts.shape[-1])
-        steps += 1
-        if time.perf_counter() - t0 >= min_seconds:
-            break
-    dt = time.perf_counter() - t0
+    affinity = len(os.sched_getaffinity(0))
+    with threadpool_limits(limits=affinity, user_api="blas"):
+        blas = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        threads = max([i.get("num_threads", 1) for i in blas] + [1])
+        steps = 0
+        t0 = time.perf_counter()
+        while True:
+            ostep.verify_step(wl.x, wl.linears, plan, wl.lm_w, wl.lm_s, drafts, 1, drafts.shape[-1])
+            steps += 1
+            if time.perf_counter() - t0 >= min_seconds:
+                break
+        dt = time.perf_counter() - t0
     step_b = sum(linear_bytes(16, k, n) for k, n, _ in plan) + lmhead_bytes(16, 2560, 151936, 15)
     gbs = step_b * steps / dt / 1e9
-    return {"value": round(gbs, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
-            "seconds": round(dt, 2), "ms_per_step": round(1e3 * dt / steps, 1),
+    return {"value": round(gbs, 4), "unit": "GB/s", "cores": threads, "affinity_cores": affinity,
+            "kind": "oracle", "seconds": round(dt, 2), "ms_per_step": round(1e3 * dt / steps, 1),
             "sample": f"{steps} whole verify steps of the same workload (36 layers x 4 linears "
                       f"at M=16, lm_head 2560->151936, greedy verify) through the numpy fp64 "
-                      f"oracle, {dt:.1f} s on {cores} threads",
+                      f"oracle, {dt:.1f} s on {threads} BLAS threads ({affinity} cores available)",
+            "c1_one_thread": c1_cpu(),
             "drafter": drafter_cpu()}
+
+
+def c1_cpu(min_seconds: float = 2.0):
+    """The oracle's block-linear verify step (one 2560 -> 2560 linear at M = 16,
+    a 4096-word int8 head with argmax, greedy verify of 15 drafts) on one thread."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    import gen
+    from oracle import step as ostep
+
+    wl = gen.make_workload(1)
+    plan = gen.chain_plan(wl.cfg)
+    drafts = np.full((1, wl.cfg.k_draft), -1, dtype=np.int32)
+    with threadpool_limits(limits=1, user_api="blas"):
+        reps = 0
+        t0 = time.perf_counter()
+        while reps < 3 or time.perf_counter() - t0 < min_seconds:
+            ostep.verify_step(wl.x, wl.linears, plan, wl.lm_w, wl.lm_s, drafts, 1, wl.cfg.k_draft)
+            reps += 1
+        dt = (time.perf_counter() - t0) / reps
+    return {"ms_per_step": round(1e3 * dt, 2), "cores": 1,
+            "sample": f"{reps} block-linear verify steps (one 2560->2560 W4A16 linear at M=16, "
+                      f"lm_head 2560->4096, greedy verify) through the numpy fp64 oracle"}
 
 
 def drafter_cpu():
@@ -115,10 +148,10 @@ def counter_traffic():
 
 def prefill(dev, reps: int = 10):
     """The prefill-shaped linears (gate+up 2560->19456, down 9728->2560) at
-    M = 2048 and 8192 through w4a16_gemm (from 33 rows on: the weights expanded to
-    fp16 by the library's kernel, then a plain fp16 GEMM): TFLOP/s per shape,
-    2*M*K*N flops over the average of ``reps`` back-to-back calls, each call
-    including its weight expansion."""
+    M = 2048 and 8192 through w4a16_gemm (from 33 rows on: the LDS-tiled MFMA
+    kernel, each 256 x 256 block tile dequantising its packed weights once into
+    LDS, split-K partials and their reduce where the plan splits): TFLOP/s per
+    shape, 2*M*K*N flops over the average of ``reps`` back-to-back calls."""
     import numpy as np
     import torch
 
@@ -417,6 +450,152 @@ def padded_batch(lins, lm_w, lm_s, steps: int = 50, warmup: int = 5):
             "mean_accepted_plus_one": round(tokens / (steps * cfg.batch), 3)}
 
 
+def c1_row(dev, reps: int = 10):
+    """The block-linear configuration: one verify step of B = 1, M = 16, K = 15
+    through one W4A16 2560 -> 2560 linear, an int8 lm_head 2560 -> 4096 with
+    fused argmax, and greedy verify.  Its 3.6 MB linear and 10.6 MB head sit
+    below the bandwidth-delay product, so both are latency-bound by design.
+    Each kernel's GB/s is taken over >= 1 GB of distinct weight copies launched
+    back to back from a HIP graph (every launch reads its weights from HBM: no
+    copy is reused within the 256 MB last-level cache); the whole step is timed
+    as graph replays with fresh drafts."""
+    import numpy as np
+    import torch
+
+    import gen
+    import w4a16_speculative_verify_amd as w4v
+    from w4a16_speculative_verify_amd.step import DeviceLinear, VerifyStep
+
+    cfg = gen.CONFIGS[1]
+    wl = gen.make_workload(1)
+    lin = wl.linears[0]
+    k, n = lin.qweight.shape[0] * 8, lin.qweight.shape[1]
+
+    def up(a):
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    x = up(wl.x)
+    qw, sc, qz = up(lin.qweight), up(lin.scales), up(lin.qzeros)
+    lin_b = linear_bytes(cfg.m, k, n)
+    n_lin = -(-(1 << 30) // lin_b)
+    copies = [(qw.clone(), sc.clone(), qz.clone()) for _ in range(n_lin)]
+    y = torch.empty((cfg.m, n), dtype=torch.float16, device=dev)
+    ws = w4v.new_workspace(max(w4v.gemm_workspace_size(cfg.m, n, k), 256), dev)
+
+    def timed_graph(fn, count):
+        fn()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fn()
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / reps / count
+
+    def all_linears():
+        for c in copies:
+            w4v.w4a16_gemm(x, *c, out=y, workspace=ws)
+
+    lin_us = timed_graph(all_linears, n_lin)
+    del copies
+    lm_w, lm_s = up(wl.lm_w), up(wl.lm_s)
+    head_b = lmhead_bytes(cfg.m, gen.HIDDEN, cfg.vocab, cfg.k_draft)
+    n_head = -(-(1 << 30) // head_b)
+    heads = [(lm_w.clone(), lm_s.clone()) for _ in range(n_head)]
+    lws = w4v.new_workspace(w4v.lmhead_workspace_size(cfg.m, gen.HIDDEN, cfg.vocab), dev)
+    t_ids = torch.empty(cfg.m, dtype=torch.int32, device=dev)
+
+    def all_heads():
+        for w, s8 in heads:
+            w4v.w8a16_lmhead_argmax(x[:, :gen.HIDDEN], w, s8, target_ids=t_ids, workspace=lws)
+
+    head_us = timed_graph(all_heads, n_head)
+    del heads
+    # the whole step, fresh drafts per replay
+    st = VerifyStep([DeviceLinear(qw, sc, qz, k, n, 1.0)], lm_w, lm_s, cfg.m, cfg.batch,
+                    cfg.k_draft)
+    none = torch.full((1, cfg.k_draft), -1, dtype=torch.int32, device=dev)
+    t0, _, _, _ = st(x, none)
+    t_host = t0.cpu().numpy()
+    drng = gen.draft_rng(1)
+    steps = 200
+    d_all = np.empty((steps, 1, cfg.k_draft), np.int32)
+    planned = np.empty(steps, np.int64)
+    for i in range(steps):
+        d_all[i], r = gen.make_drafts(drng, cfg, t_host)
+        planned[i] = r[0]
+    d_dev, d_buf = up(d_all), torch.empty((1, cfg.k_draft), dtype=torch.int32, device=dev)
+    acc = torch.zeros(steps, dtype=torch.int32, device=dev)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        st(x, d_buf)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        st(x, d_buf)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(steps):
+        d_buf.copy_(d_dev[i], non_blocking=True)
+        g.replay()
+        acc[i:i + 1].copy_(st.accepted_len, non_blocking=True)
+    e1.record()
+    torch.cuda.synchronize()
+    step_us = e0.elapsed_time(e1) * 1e3 / steps
+    a = acc.cpu().numpy().astype(np.int64)
+    if not np.array_equal(a, planned):
+        raise RuntimeError("block-linear step: accepted lengths differ from the planned ones")
+    tokens = int(np.sum(a + 1))
+    return {"workload": "block-linear verify step M=16 (K=15): W4A16 g128 2560->2560 + int8 "
+                        "lm_head 2560->4096 with fused argmax + greedy verify",
+            "gemm_us": round(lin_us, 3), "gemm_bytes": lin_b,
+            "gemm_gbs": round(lin_b / (lin_us * 1e-6) / 1e9, 1),
+            "gemm_pct_of_hbm_peak": round(100 * lin_b / (lin_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 2),
+            "gemm_copies": n_lin,
+            "lmhead_us": round(head_us, 3), "lmhead_bytes": head_b,
+            "lmhead_gbs": round(head_b / (head_us * 1e-6) / 1e9, 1),
+            "lmhead_copies": n_head,
+            "step_us": round(step_us, 2),
+            "verified_tokens_per_s": round(tokens / (step_us * steps / 1e6), 1),
+            "mean_accepted_plus_one": round(tokens / steps, 3)}
+
+
+def chain_linears(lins, x, reps: int = 20):
+    """The same 144 linears in one persistent launch (w4a16_chain): each CU's
+    share of every linear streamed into LDS ahead of the math, ready flags
+    between the linears.  Average of ``reps`` launches; GB/s over the same
+    algorithmic bytes as the per-launch path."""
+    import torch
+    import w4a16_speculative_verify_amd as w4v
+
+    ch = w4v.Chain([(l.qweight, l.scales, l.qzeros, l.alpha) for l in lins], x.shape[0], x.device)
+    y = torch.empty((x.shape[0], lins[-1].n_out), dtype=torch.float16, device=x.device)
+    for _ in range(3):
+        ch(x, out=y)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        ch(x, out=y)
+    e1.record()
+    torch.cuda.synchronize()
+    if ch.error() != 0:
+        raise RuntimeError(f"chain error word {ch.error()}")
+    us = e0.elapsed_time(e1) * 1e3 / reps
+    b = sum(linear_bytes(x.shape[0], l.k_in, l.n_out) for l in lins)
+    del ch
+    return {"us": round(us, 2), "gbs": round(b / (us * 1e-6) / 1e9, 1),
+            "pct_of_hbm_peak": round(100 * b / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 2)}
+
+
 def drafter(dev, reps: int = 200):
     """Prompt-lookup drafting ahead of the verify (not part of the timed step):
     ngram_draft over B synthetic histories of 8192 tokens (half copied spans),
@@ -480,6 +659,8 @@ def main():
                     help="one device-to-device copy of this many MiB before timing (counter calibration)")
     ap.add_argument("--path", choices=["chain", "per-linear"], default="per-linear",
                     help="one persistent launch for all linears, or one launch per linear")
+    ap.add_argument("--no-chain", action="store_true",
+                    help="skip the one-launch chain timing of the same linears")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -560,16 +741,18 @@ def main():
     torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    ev0.record(stream)
-    for i in range(args.warmup, total):
+    evs[0].record(stream)
+    for j, i in enumerate(range(args.warmup, total)):
         one_step(i)
-    ev1.record(stream)
+        evs[j + 1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    step_ms = ev0.elapsed_time(ev1) / args.steps
+    step_ms = evs[0].elapsed_time(evs[-1]) / args.steps
+    per_step = np.array([evs[j].elapsed_time(evs[j + 1]) for j in range(args.steps)])
+    p10, p50, p90 = (float(np.percentile(per_step, q)) for q in (10, 50, 90))
 
     acc = acc_hist.cpu().numpy().astype(np.int64)
     if not np.array_equal(acc, planned):
@@ -595,6 +778,18 @@ def main():
     act_launch_us = lin_ms * 1e3 / n_launch
     gemm_gbs = lin_b / (lin_ms / 1e3) / 1e9
     step_gbs = (lin_b + lm_b) / (step_ms / 1e3) / 1e9
+
+    c1 = None
+    if not args.no_other_m:
+        print("[bench] timing the block-linear configuration (M = 16, one linear, 4096-word head)",
+              file=sys.stderr, flush=True)
+        c1 = c1_row(dev)
+
+    chain = None
+    if not args.no_chain and args.path != "chain":
+        print("[bench] timing the same linears in one persistent launch", file=sys.stderr,
+              flush=True)
+        chain = chain_linears(lins, x)
 
     m1 = padded = None
     if not args.no_other_m:
@@ -643,6 +838,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(step_ms, 4),
+        "ms_per_step_p10_p50_p90": [round(p10, 4), round(p50, 4), round(p90, 4)],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -668,6 +864,8 @@ def main():
                      "bytes_per_launch": round(lin_b / n_launch),
                      "avg_launch_us": round(act_launch_us, 3)},
         "cpu_baseline": cpu,
+        "block_linear_c1": c1,
+        "linears_one_launch_chain": chain,
         "prefill": pre,
         "decode_m1": m1,
         "padded_batch_m168": padded,
