@@ -15,7 +15,16 @@
 //            it row-contiguous (4 rows x 256 bytes per instruction, 4/WT
 //            instructions each), reorder each 8-k chunk to the k order of the
 //            dequantised nibbles and store it in a double-buffered LDS tile,
-//            from which every wave reads the MFMA A layout.
+//            from which every wave reads the MFMA A layout.  With one tile
+//            per block no other wave reads a k-slice's tile, so the step
+//            takes no block barrier (a wave's LDS accesses complete in
+//            order).  A single activation row (DX) skips LDS: each lane loads
+//            its A fragments straight from memory (four distinct 16-byte
+//            pieces per instruction, all lanes reading row 0) and reorders
+//            them in registers.  Measured per 144-linear step: the barrier
+//            dropped for one-tile blocks, 1,173 -> 1,150 us at M = 16; direct
+//            fragments at M = 1, 1,081 -> 1,060 us (at M = 16 they touch 16
+//            rows per instruction and were slower, 1,179 us).
 // Loads run D groups ahead of the math (a ring of register sets), and every
 // load is unconditional (a missing group reads zeros from outside its buffer
 // resource), because a load under a branch makes the compiler wait for all
@@ -117,11 +126,12 @@ __device__ __forceinline__ void store_row4(_Float16* dst, float a0, float a1, fl
 // stride, the split parameters): the library builds this kernel with those 14
 // dwords preloaded into SGPRs, so the prologue's loads issue without waiting
 // for argument loads; the rest of GemmArgs is needed only by the epilogue.
-template <int MT, int WT, int WK, int D, int SB, int Q>
+template <int MT, int WT, int WK, int D, int SB, int Q, int DX>
 __global__ __launch_bounds__(64 * WT * WK) void w4a16_skinny_kernel(
     const uint32_t* pqw, const _Float16* psc, const uint32_t* pqz, const _Float16* px, int pN,
     int pM, int pldx, int splits, int gbase, int grem, GemmArgs a, unsigned* tickets,
     float* partials) {
+  static_assert(!DX || (MT == 1 && WT == 1), "direct fragments: one row tile, one tile");
   constexpr int NW = WT * WK;                       // waves per block
   constexpr int kXWords = MT * 16 * kXRowWords;     // one group's activation tile
   const int lane = threadIdx.x & 63;
@@ -154,7 +164,7 @@ __global__ __launch_bounds__(64 * WT * WK) void w4a16_skinny_kernel(
   const int col = colok ? col_raw : pN - 4;         // the column this lane reads
 
   constexpr int E = MT * 16;                        // accumulator floats per lane
-  constexpr int kTileWords = 2 * WK * kXWords;      // double-buffered activation tiles
+  constexpr int kTileWords = DX ? 0 : 2 * WK * kXWords;   // double-buffered activation tiles
   constexpr int kRedWords = (WK > 1) ? NW * E * 64 : 0;
   __shared__ uint32_t lds[kTileWords > kRedWords ? kTileWords : kRedWords];
   auto xtile = [&](int buf, int slice) { return lds + (buf * WK + slice) * kXWords; };
@@ -183,9 +193,16 @@ __global__ __launch_bounds__(64 * WT * WK) void w4a16_skinny_kernel(
   o.gs = N * 2;
 #pragma unroll
   for (int q = 0; q < Frag<MT, WT, Q>::kXLoads; ++q) {
-    int m = mbase + xrow_of(q * WT + wt, lane);
-    m = m < pM ? m : pM - 1;                        // rows past M: never stored
-    o.x[q] = ((uint32_t)m * (uint32_t)pldx + chunk * 8) * 2;
+    if constexpr (DX) {
+      // A fragment q = it: row l % 16 (row 0 when M = 1), k = 32 it + 8 (l / 16) .. + 7
+      int m = mbase + chunk;
+      m = m < pM ? m : pM - 1;                      // rows past M: never stored
+      o.x[q] = ((uint32_t)m * (uint32_t)pldx + q * 32 + kb * 8) * 2;
+    } else {
+      int m = mbase + xrow_of(q * WT + wt, lane);
+      m = m < pM ? m : pM - 1;                      // rows past M: never stored
+      o.x[q] = ((uint32_t)m * (uint32_t)pldx + chunk * 8) * 2;
+    }
   }
   // prologue loads in the loop's order (f[0] complete, then f[1], ...): the
   // wait counts at the loop head are then the same on entry and on the back edge
@@ -215,13 +232,16 @@ __global__ __launch_bounds__(64 * WT * WK) void w4a16_skinny_kernel(
   auto step = [&](auto slot, const int j) __attribute__((always_inline)) {
     constexpr int i = decltype(slot)::value;
     // share the group's activations: this wave's chunks, reordered to the
-    // k order of the dequantised nibbles, into the LDS tile
+    // k order of the dequantised nibbles, into the LDS tile (the waves of
+    // both tiles of a k-slice read it: a block barrier with two tiles)
     uint32_t* xt = xtile(j & 1, wk);
+    if constexpr (!DX) {
 #pragma unroll
-    for (int q = 0; q < Frag<MT, WT, Q>::kXLoads; ++q)
-      *reinterpret_cast<f16x8*>(xt + xrow_of(q * WT + wt, lane) * kXRowWords + chunk * 4) =
-          permute_for_int4(f[i].x[q]);
-    lds_barrier();
+      for (int q = 0; q < Frag<MT, WT, Q>::kXLoads; ++q)
+        *reinterpret_cast<f16x8*>(xt + xrow_of(q * WT + wt, lane) * kXRowWords + chunk * 4) =
+            permute_for_int4(f[i].x[q]);
+      if constexpr (WT > 1) lds_barrier();
+    }
     if (j < n) {                                  // wave-uniform
       // per quantisation group: exact fp16 (q - z) operands, the group's
       // fp32 sum over its 128 / Q k, then its scale once
@@ -240,9 +260,13 @@ __global__ __launch_bounds__(64 * WT * WK) void w4a16_skinny_kernel(
           // A layout: row l % 16, k = 32 it + 8 (l / 16) .. + 7
           f16x8 av[MT];
 #pragma unroll
-          for (int mt = 0; mt < MT; ++mt)
-            av[mt] = *reinterpret_cast<const f16x8*>(xt + (mt * 16 + chunk) * kXRowWords +
-                                                     (it * 4 + kb) * 4);
+          for (int mt = 0; mt < MT; ++mt) {
+            if constexpr (DX)
+              av[mt] = permute_for_int4(f[i].x[it]);
+            else
+              av[mt] = *reinterpret_cast<const f16x8*>(xt + (mt * 16 + chunk) * kXRowWords +
+                                                       (it * 4 + kb) * 4);
+          }
 #pragma unroll
           for (int c = 0; c < 4; ++c) {
             const f16x8 b = dequant_int4_word(f[i].w[it][c], zz[c], magic);
@@ -388,11 +412,11 @@ __global__ __launch_bounds__(64 * WT * WK) void w4a16_skinny_kernel(
   }
 }
 
-template <int MT, int WT, int WK, int D, int SB, int Q>
+template <int MT, int WT, int WK, int D, int SB, int Q, int DX>
 void launch_t(const GemmArgs& a, const GemmPlan& p, unsigned* tickets, float* partials,
               hipStream_t stream) {
   const int G = a.K / kGroup;
-  hipLaunchKernelGGL((w4a16_skinny_kernel<MT, WT, WK, D, SB, Q>),
+  hipLaunchKernelGGL((w4a16_skinny_kernel<MT, WT, WK, D, SB, Q, DX>),
                      dim3(p.col_blocks, p.splits, p.mblocks), dim3(64 * WT * WK), 0, stream,
                      a.qweight, a.scales, a.qzeros, a.x, a.N, a.M, (int)a.ldx, p.splits,
                      G / p.splits, G % p.splits, a, tickets, partials);
@@ -400,18 +424,28 @@ void launch_t(const GemmArgs& a, const GemmPlan& p, unsigned* tickets, float* pa
 
 // Four k-slices per block, one or two tiles, three steps in flight per wave;
 // one batch of partial loads up to 8 splits, batches of 16 beyond.
-template <int MT, int WT, int Q>
+template <int MT, int WT, int Q, int DX>
 void launch_w(const GemmArgs& a, const GemmPlan& p, unsigned* tickets, float* partials,
               hipStream_t stream) {
-  if (p.splits <= 8) launch_t<MT, WT, 4, 3, 8, Q>(a, p, tickets, partials, stream);
-  else launch_t<MT, WT, 4, 3, 16, Q>(a, p, tickets, partials, stream);
+  if (p.splits <= 8) launch_t<MT, WT, 4, 3, 8, Q, DX>(a, p, tickets, partials, stream);
+  else launch_t<MT, WT, 4, 3, 16, Q, DX>(a, p, tickets, partials, stream);
 }
 
+// a single activation row on one-tile blocks takes its A fragments directly
 template <int MT, int Q>
 void launch_q(const GemmArgs& a, const GemmPlan& p, unsigned* tickets, float* partials,
               hipStream_t stream) {
-  if (p.wt == 1) launch_w<MT, 1, Q>(a, p, tickets, partials, stream);
-  else launch_w<MT, 2, Q>(a, p, tickets, partials, stream);
+  if (p.wt == 1) {
+    if constexpr (MT == 1) {
+      if (a.M == 1) {
+        launch_w<1, 1, Q, 1>(a, p, tickets, partials, stream);
+        return;
+      }
+    }
+    launch_w<MT, 1, Q, 0>(a, p, tickets, partials, stream);
+  } else {
+    launch_w<MT, 2, Q, 0>(a, p, tickets, partials, stream);
+  }
 }
 
 }  // namespace
