@@ -82,7 +82,7 @@ int w4v_abi_version(void);
  *          scale applied to that group's fp32 sum (split-K across blocks).
  *          M >= 33 (the batched verify block, prefill shapes: bound by the
  *          matrix cores): an LDS-tiled MFMA kernel that dequantises each
- *          256-column x 64-k weight tile once per 256-row block tile, as
+ *          256-column x 32-k weight tile once per 256-row block tile, as
  *          w = fp16_rne(s * (q - z)) (q - z exact, one rounding; the fp32
  *          accumulation and the alpha / output rounding as above); shapes with
  *          few block tiles are split along K with fp32 partials in the

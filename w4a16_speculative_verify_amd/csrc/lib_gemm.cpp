@@ -1,6 +1,6 @@
-// Plain fp16 GEMM through hipBLASLt: the prefill-shaped W4A16 linear (after
-// the weights were dequantised by this library's own kernel) and the
-// half-precision linears of a partly quantised target.
+// Plain fp16 GEMM through hipBLASLt: the half-precision linears of a partly
+// quantised target (results page section 5: layers kept in fp16).  No W4A16
+// call goes through it.
 //
 //   y[M x N] (row-major, ldy) = alpha * x[M x K] (row-major, ldx) @ wt[N x K]^T (ldw)
 //
