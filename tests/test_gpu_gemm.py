@@ -20,7 +20,9 @@ def run_gemm(w4v, x, lin, alpha=1.0, ws=None, no_ws=False):
 
 @pytest.mark.parametrize("m,k,n", [
     (16, 2560, 2560),          # block linear at M = 16
-    (1, 2560, 2560),
+    (1, 2560, 2560),           # one row: A fragments straight from memory
+    (1, 9728, 2560),           # one row, deep K (split across blocks)
+    (1, 2560, 19456),          # one row, two tiles per block (LDS-staged activations)
     (5, 384, 200),             # ragged N (not a multiple of 64)
     (16, 1280, 72),
     (21, 1280, 520),           # M = K+1 with K = 20: two m-tiles, ragged rows
@@ -86,7 +88,7 @@ def test_mfma_split_plan_requires_its_workspace(lib):
 
 
 @pytest.mark.parametrize("enc", range(3))
-@pytest.mark.parametrize("m", [16, 21, 64, 200, 640])
+@pytest.mark.parametrize("m", [1, 16, 21, 64, 200, 640])
 def test_identity_weights_bit_exact(lib, enc, m):
     n = 512
     eye = np.eye(n, dtype=np.int64)

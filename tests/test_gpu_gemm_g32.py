@@ -46,7 +46,7 @@ def test_random_shapes_group_32(lib, m, k, n):
 
 
 @pytest.mark.parametrize("enc", range(3))
-@pytest.mark.parametrize("m", [16, 21, 64, 200, 640])
+@pytest.mark.parametrize("m", [1, 16, 21, 64, 200, 640])
 def test_identity_weights_bit_exact_group_32(lib, enc, m):
     """q - z in {0, 1} (or {0, 2} at scale 0.5) with the zero-point changing every 32 k."""
     n = 512

@@ -43,6 +43,24 @@ def test_random(lib, m, v):
     log(f"  low-margin rows {low}/{m}")
 
 
+# Blocks of at most 16 rows stage the whole hidden rows in LDS when H <= 2560 (the
+# swizzled tile, fewer 128-k segments than the tile holds at small H); wider rows take
+# the per-step hidden tile.  Both sides of that switch, one row and sixteen.
+@pytest.mark.parametrize("m,h,v", [(16, 128, 700), (1, 1024, 3000), (16, 2432, 2100),
+                                   (16, 2688, 3000), (1, 4096, 1500), (12, 5120, 900)])
+def test_hidden_widths(lib, m, h, v):
+    log(f"lmhead m={m} h={h} v={v}")
+    rng = np.random.default_rng(7 * m + h + v)
+    w8 = gen.lmhead_weights(rng, v, h)
+    s8 = gen.lmhead_scales(rng, v)
+    x = gen.activations(rng, m, h)
+    t, mx = run_lm(lib, x, w8, s8)
+    lg = olm.logits(x, w8, s8)
+    low, t_o, top, _ = check_argmax(t, lg, f"m={m} h={h} v={v}")
+    sure = np.flatnonzero(t == t_o)
+    assert np.allclose(mx[sure], top[sure], rtol=1e-5, atol=1e-4)
+
+
 @pytest.mark.parametrize("m", [16, 100])
 def test_ties_go_to_lowest_index(lib, m):
     rng = np.random.default_rng(5 + m)
