@@ -458,7 +458,7 @@ def c1_row(dev, reps: int = 10):
     Each kernel's GB/s is taken over >= 1 GB of distinct weight copies launched
     back to back from a HIP graph (every launch reads its weights from HBM: no
     copy is reused within the 256 MB last-level cache); the whole step is timed
-    as graph replays with fresh drafts."""
+    as 200 consecutive steps with fresh drafts captured in one HIP graph."""
     import numpy as np
     import torch
 
@@ -538,15 +538,21 @@ def c1_row(dev, reps: int = 10):
         st(x, d_buf)
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
+    # all the steps in one graph (each: its drafts copied in, the step, its
+    # accepted length copied out), so that the host's per-replay launch cost,
+    # larger than this step, does not set the time
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
-        st(x, d_buf)
+        for i in range(steps):
+            d_buf.copy_(d_dev[i], non_blocking=True)
+            st(x, d_buf)
+            acc[i:i + 1].copy_(st.accepted_len, non_blocking=True)
+    g.replay()
+    torch.cuda.synchronize()
+    acc.zero_()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
-    for i in range(steps):
-        d_buf.copy_(d_dev[i], non_blocking=True)
-        g.replay()
-        acc[i:i + 1].copy_(st.accepted_len, non_blocking=True)
+    g.replay()
     e1.record()
     torch.cuda.synchronize()
     step_us = e0.elapsed_time(e1) * 1e3 / steps
