@@ -1,8 +1,9 @@
 // Greedy prefix acceptance ("Efficient LLM Challenge Results", section 3:
 // drafts are kept only as far as each one equals the token the target picks
 // greedily after the drafts before it; -1 padding can never equal a
-// vocabulary id, so padding never extends the accepted run).  One thread per sequence; the scan stops at the first
-// draft that is out of [0, V) or differs from the target's token.
+// vocabulary id, so padding never extends the accepted run).  One thread per
+// sequence; the scan stops at the first draft that is out of [0, V) or
+// differs from the target's token.
 #include "w4v_launch.h"
 
 namespace w4v {
