@@ -99,6 +99,11 @@ int w4v_abi_version(void);
  *          the result does not depend on the order in which they arrive.  One
  *          workspace sized for the largest call serves calls of every shape
  *          ordered on one stream.
+ * Placement  the first M <= 32 call with a K-split on a device, outside
+ *          stream capture, launches a small probe of how the device deals
+ *          blocks to its XCDs and waits for `stream` once; when blocks whose
+ *          ids agree mod 8 share an XCD, later calls keep the split-K
+ *          hand-off in that XCD's L2 (same result bits either way).
  * ---------------------------------------------------------------------- */
 size_t w4a16_gemm_workspace_size(int M, int N, int K, int group_size);
 

@@ -36,6 +36,7 @@ struct GemmArgs {
   int M, N, K;
   float alpha;
   int group_size;    // 128, or 32 (four quantisation groups per 128-k step)
+  int xcd_local;     // set by the launcher: blocks with ids equal mod 8 share an XCD
 };
 
 struct GemmPlan {
