@@ -97,6 +97,7 @@ struct LmheadPlan {
   int tiles;         // 16-row vocabulary tiles per wave pass (1 or 2)
   int depth;         // steps in flight per wave (3)
   int vblocks;       // blocks along the vocabulary
+  int waves;         // waves per block (4, or 8 for two 96-row blocks)
   size_t ticket_bytes;
   size_t partial_bytes;
   size_t workspace_bytes() const { return ticket_bytes + partial_bytes; }

@@ -9,10 +9,10 @@
 //     8-byte slice is the B operand of one 16x16x32 MFMA.  With fp16 weights
 //     (a half-precision head) the lane streams 64 bytes, four 128-bit loads,
 //     each the B operand of one MFMA as loaded.
-//   A (hidden rows) = one 128-k chunk per step, loaded once per block (one
-//     16-byte load per thread) into a double-buffered LDS tile that the four
-//     waves share: per-wave loads of it would cost a CU as much load
-//     throughput as half the weights.  A block of at most 16 rows with
+//   A (hidden rows) = one 128-k chunk per step, loaded once per block (16
+//     bytes per thread and load round) into a double-buffered LDS tile that
+//     the block's waves share: per-wave loads of it would cost a CU as much
+//     load throughput as half the weights.  A block of at most 16 rows with
 //     H <= kWholeH instead stages the whole hidden rows in LDS once, before
 //     its first step (80 KiB at H = 2560): the steps then need no hidden
 //     loads, no LDS writes and no barrier.  Its 16-byte chunks are swizzled
@@ -41,8 +41,6 @@ namespace w4v {
 
 namespace {
 
-constexpr int kWaves = 4;
-constexpr int kThreads = 64 * kWaves;
 constexpr int kChunk = 128;                         // k per step
 constexpr int kHRowWords = (kChunk * 2 + 16) / 4;   // padded LDS row of the hidden chunk
 constexpr int kLmheadBlocksPerCU = 1;
@@ -63,19 +61,27 @@ __device__ __forceinline__ void shfl_best(float& v, int& i, int mask) {
 
 // F16 = 0: int8 weights with one fp16 scale per vocabulary row; F16 = 1: fp16
 // weights, no scale (a half-precision lm_head, results page section 5).
-template <int MT, int TILES, int F16, int WH>
+template <int MT, int TILES, int F16, int WH, int HR>
 struct Step {
   static constexpr int kLoads = F16 ? 4 : 2;      // 128-bit loads per tile row (32 k)
   u32x4 w[TILES][kLoads];  // 32 k of each tile row
-  u32x4 h[WH ? 1 : MT];    // this thread's 16 bytes of the hidden chunk (not with WH)
+  u32x4 h[WH ? 1 : HR];    // this thread's 16-byte pieces of the hidden chunk (not with WH)
   uint32_t sc[TILES];      // fp16 scale of each tile row (int8 only; with a pass's last step)
 };
 
-// WH = 1: 16-row block (MT = 1) with the whole hidden rows in LDS, H <= kWholeH
-template <int MT, int TILES, int D, int F16, int WH>
-__global__ __launch_bounds__(kThreads) void lmhead_argmax_kernel(LmheadArgs a, unsigned* ticket,
-                                                                 float* pval, int* pidx) {
-  static_assert(!WH || MT == 1, "whole hidden rows only for 16-row blocks");
+// WH = 1: 16-row block (MT = 1) with the whole hidden rows in LDS, H <= kWholeH.
+// NW waves per block (4, or 8 for 96-row blocks: the hidden chunk, which every
+// step loads whole, then serves twice as many vocabulary rows).
+template <int MT, int TILES, int D, int F16, int WH, int NW>
+__global__ __launch_bounds__(64 * NW) void lmhead_argmax_kernel(LmheadArgs a, unsigned* ticket,
+                                                                float* pval, int* pidx) {
+  static_assert(!WH || (MT == 1 && NW == 4), "whole hidden rows only for 16-row blocks");
+  constexpr int kWaves = NW;
+  constexpr int kThreads = 64 * NW;
+  // hidden chunk: each load round covers 4 NW rows (16 threads per row)
+  constexpr int kRowsPerRound = kThreads / 16;
+  static_assert((16 * MT) % kRowsPerRound == 0, "hidden rows must fill the load rounds");
+  constexpr int HR = 16 * MT / kRowsPerRound;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int kb = lane >> 4;
@@ -100,14 +106,14 @@ __global__ __launch_bounds__(kThreads) void lmhead_argmax_kernel(LmheadArgs a, u
   const rsrc_t rw = make_rsrc(a.w);
   const rsrc_t rh = make_rsrc(a.h);
   const rsrc_t rs = make_rsrc(a.scales);
-  // hidden chunk: thread t loads row t / 16 (+16 per m-tile), 8 k at (t % 16) * 8
+  // hidden chunk: thread t loads row t / 16 (+4 NW per round), 8 k at (t % 16) * 8
   const int hr = threadIdx.x >> 4, hc = threadIdx.x & 15;
-  uint32_t hoff[MT];
+  uint32_t hoff[HR];
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-    int m = mbase + mt * 16 + hr;
+  for (int j = 0; j < HR; ++j) {
+    int m = mbase + j * kRowsPerRound + hr;
     m = m < a.M ? m : a.M - 1;                     // rows past M: never reported
-    hoff[mt] = ((uint32_t)m * (uint32_t)a.ldh + hc * 8) * 2;
+    hoff[j] = ((uint32_t)m * (uint32_t)a.ldh + hc * 8) * 2;
   }
   // lane row of tile t in pass p; rows past the block's share load nothing
   auto row_of = [&](int pass, int t) {
@@ -115,7 +121,7 @@ __global__ __launch_bounds__(kThreads) void lmhead_argmax_kernel(LmheadArgs a, u
   };
 
   constexpr int EB = F16 ? 2 : 1;                   // bytes per weight
-  auto load_step = [&](Step<MT, TILES, F16, WH>& f, int st) {
+  auto load_step = [&](Step<MT, TILES, F16, WH, HR>& f, int st) {
     // Offsets are masked by OR-ing kNoLoad (bit 31) in, never by choosing
     // between two loads: the compiler turns a select on a block-uniform
     // condition into a branch around the load.
@@ -130,11 +136,11 @@ __global__ __launch_bounds__(kThreads) void lmhead_argmax_kernel(LmheadArgs a, u
           (((uint32_t)(v < vb1 ? v : 0) * (uint32_t)a.H + kb * 32 + ch * kChunk) * EB) | skip |
           (v < vb1 ? 0u : kNoLoad);
 #pragma unroll
-      for (int u = 0; u < Step<MT, TILES, F16, WH>::kLoads; ++u) f.w[t][u] = ld_x4(rw, off + 16 * u);
+      for (int u = 0; u < Step<MT, TILES, F16, WH, HR>::kLoads; ++u) f.w[t][u] = ld_x4(rw, off + 16 * u);
     }
     if constexpr (!WH) {
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) f.h[mt] = ld_x4(rh, (hoff[mt] + ch * kChunk * 2) | skip);
+      for (int j = 0; j < HR; ++j) f.h[j] = ld_x4(rh, (hoff[j] + ch * kChunk * 2) | skip);
     }
     // the row scales ride with the last step of a pass (a load at the pass end
     // would wait for the whole ring)
@@ -174,7 +180,7 @@ __global__ __launch_bounds__(kThreads) void lmhead_argmax_kernel(LmheadArgs a, u
     for (int j = 0; j < kWholeLoads; ++j)
       hw[j] = ld_x4(rh, (hoff[0] + (uint32_t)j * kChunk * 2) | (j < nchunks ? 0u : kNoLoad));
   }
-  Step<MT, TILES, F16, WH> f[D];
+  Step<MT, TILES, F16, WH, HR> f[D];
   // prologue in the loop's order, so the loop head's wait counts agree on entry
 #pragma unroll
   for (int i = 0; i < D; ++i) {
@@ -200,8 +206,9 @@ __global__ __launch_bounds__(kThreads) void lmhead_argmax_kernel(LmheadArgs a, u
       uint32_t* ht = hbuf + (st & 1) * kHWords;
       if constexpr (!WH) {
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-          *reinterpret_cast<u32x4*>(ht + (mt * 16 + hr) * kHRowWords + hc * 4) = f[i].h[mt];
+        for (int j = 0; j < HR; ++j)
+          *reinterpret_cast<u32x4*>(ht + (j * kRowsPerRound + hr) * kHRowWords + hc * 4) =
+              f[i].h[j];
         lds_barrier();
       }
       // whole-row tile: this step's 128-k segment
@@ -342,15 +349,15 @@ __global__ __launch_bounds__(kThreads) void lmhead_argmax_kernel(LmheadArgs a, u
   }
 }
 
-template <int MT, int TILES, int WH>
+template <int MT, int TILES, int WH, int NW>
 void launch_h(const LmheadArgs& a, const LmheadPlan& p, unsigned* ticket, float* pval, int* pidx,
               hipStream_t stream) {
   if (a.f16)
-    hipLaunchKernelGGL((lmhead_argmax_kernel<MT, TILES, 3, 1, WH>), dim3(p.mblocks, p.vblocks),
-                       dim3(kThreads), 0, stream, a, ticket, pval, pidx);
+    hipLaunchKernelGGL((lmhead_argmax_kernel<MT, TILES, 3, 1, WH, NW>),
+                       dim3(p.mblocks, p.vblocks), dim3(64 * NW), 0, stream, a, ticket, pval, pidx);
   else
-    hipLaunchKernelGGL((lmhead_argmax_kernel<MT, TILES, 3, 0, WH>), dim3(p.mblocks, p.vblocks),
-                       dim3(kThreads), 0, stream, a, ticket, pval, pidx);
+    hipLaunchKernelGGL((lmhead_argmax_kernel<MT, TILES, 3, 0, WH, NW>),
+                       dim3(p.mblocks, p.vblocks), dim3(64 * NW), 0, stream, a, ticket, pval, pidx);
 }
 
 template <int MT, int TILES>
@@ -358,11 +365,17 @@ void launch_t(const LmheadArgs& a, const LmheadPlan& p, unsigned* ticket, float*
               hipStream_t stream) {
   if constexpr (MT == 1) {
     if (a.H <= kWholeH) {
-      launch_h<1, TILES, 1>(a, p, ticket, pval, pidx, stream);
+      launch_h<1, TILES, 1, 4>(a, p, ticket, pval, pidx, stream);
       return;
     }
   }
-  launch_h<MT, TILES, 0>(a, p, ticket, pval, pidx, stream);
+  if constexpr (MT == 6) {
+    if (p.waves == 8) {
+      launch_h<6, TILES, 0, 8>(a, p, ticket, pval, pidx, stream);
+      return;
+    }
+  }
+  launch_h<MT, TILES, 0, 4>(a, p, ticket, pval, pidx, stream);
 }
 
 }  // namespace
@@ -372,7 +385,8 @@ LmheadPlan plan_lmhead(int M, int H, int V, int num_cus) {
   LmheadPlan p{};
   // rows per block: 16, 32, 64, then 96 (a batched verify block of 8 x 21 rows
   // takes two blocks of 96 per vocabulary share; measured on MI355X at M = 168:
-  // 299 us against 344 us with 64-row blocks and 454 us with 32-row blocks)
+  // 299 us against 344 us with 64-row blocks and 454 us with 32-row blocks,
+  // all with four waves per block)
   p.mt = (M <= 16) ? 1 : (M <= 32 ? 2 : (M <= 64 ? 4 : 6));
   p.mblocks = (M + 16 * p.mt - 1) / (16 * p.mt);
   // 32 rows per wave pass when the vocabulary fills the chip, else 16 (two
@@ -381,9 +395,14 @@ LmheadPlan plan_lmhead(int M, int H, int V, int num_cus) {
   // among one block per CU
   p.tiles = ((long)V >= 32L * 4 * num_cus) ? 2 : 1;
   p.depth = 3;
-  const int rows_per_pass = kWaves * p.tiles * 16;
+  // two 96-row blocks: eight waves each (256 vocabulary rows per pass, so the
+  // hidden chunk that each step loads whole serves twice as many weight
+  // rows), one block per CU: 257 against 301 us at M = 168 on MI355X
+  p.waves = (p.mt == 6 && p.mblocks == 2) ? 8 : 4;
+  const int rows_per_pass = p.waves * p.tiles * 16;
   const int npasses = (V + rows_per_pass - 1) / rows_per_pass;
-  p.vblocks = npasses < kLmheadBlocksPerCU * num_cus ? npasses : kLmheadBlocksPerCU * num_cus;
+  const int per_cu = p.waves == 8 ? num_cus / p.mblocks : kLmheadBlocksPerCU * num_cus;
+  p.vblocks = npasses < per_cu ? npasses : per_cu;
   const size_t nblocks = (size_t)p.vblocks * p.mblocks;
   p.ticket_bytes = kTicketRegion;
   p.partial_bytes = align_up(nblocks * 16 * p.mt * sizeof(float), kWorkspaceAlign) +
@@ -399,7 +418,9 @@ hipError_t launch_lmhead_argmax(const LmheadArgs& a, const LmheadPlan& p, void* 
   float* pval = reinterpret_cast<float*>(base);
   int* pidx = reinterpret_cast<int*>(base + align_up(nblocks * 16 * p.mt * sizeof(float),
                                                      kWorkspaceAlign));
-  if (p.depth != 3 || (p.tiles != 1 && p.tiles != 2)) return hipErrorInvalidValue;
+  if (p.depth != 3 || (p.tiles != 1 && p.tiles != 2) || (p.waves != 4 && p.waves != 8) ||
+      (p.waves == 8 && p.mt != 6))
+    return hipErrorInvalidValue;
   if (p.mt == 1) {
     if (p.tiles == 2) launch_t<1, 2>(a, p, ticket, pval, pidx, stream);
     else launch_t<1, 1>(a, p, ticket, pval, pidx, stream);
