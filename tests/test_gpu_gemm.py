@@ -54,6 +54,8 @@ def test_random_shapes(lib, m, k, n):
     (300, 1280, 1032),
     (128, 128, 128),           # exactly one stage pair, one group
     (168, 2560, 2560),         # the padded verify batch of 8 x 21 rows
+    (97, 512, 264),            # 128-row block tiles, ragged rows
+    (192, 384, 256),           # 192-row block tiles, every row present
     (600, 1280, 520),
     (257, 4096, 264),          # one row and 8 columns past a 256 x 256 tile
 ])

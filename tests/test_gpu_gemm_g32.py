@@ -30,6 +30,7 @@ def run_gemm(w4v, x, lin, alpha=1.0, ws=None, no_ws=False):
     (5, 128, 8),               # one 128-k step, four groups, narrowest N
     (33, 256, 200),            # the M >= 33 kernel, ragged rows and columns
     (200, 1280, 1032),
+    (150, 1280, 520),          # 192-row block tiles
     (512, 384, 136),
     (640, 1280, 1032),
 ])

@@ -4,13 +4,14 @@
 // bucket's cost is prefill compute), so the 4-bit weights are dequantised
 // once per block tile into LDS and shared by all of the tile's rows.
 //
-// Block tile 256 rows x 256 columns, 32 k per stage.  Every global load is an
+// Block tile 256 rows x 256 columns (128 or 192 rows for calls with no more
+// rows than that), 32 k per stage.  Every global load is an
 // LDS DMA (buffer_load ... lds: no registers; issued from inline assembly so
 // that the compiler does not wait for it at unrelated LDS accesses -- the
 // kernel waits itself with explicit vmcnt counts), kSlots stages deep in a
-// ring of LDS slots, so that a stage's data has three stages of MFMA time to
+// ring of LDS slots (5, or 7 / 9 with the smaller tiles), so that a stage's data has several stages of MFMA time to
 // arrive.  A slot holds one stage's
-//   A     256 rows x 32 k fp16, row r's 16-byte chunk c stored at
+//   A     the tile's rows x 32 k fp16, row r's 16-byte chunk c stored at
 //         r * 4 + (c ^ lds_sw4(r));
 //   W     the packed words, 4 packed rows x 256 columns;
 //   meta  the stage's quantisation group: 256 fp16 scales, 32 zero words.
@@ -21,7 +22,8 @@
 // position v = 64 g + 16 c + j, its chunk c' at v * 4 + (c' ^ lds_sw4(v)).
 // The row swizzle lds_sw4 (w4v_device.h) keeps the MFMA operand reads and
 // the dequantisation writes free of LDS bank conflicts.
-// 8 waves as 2 (rows) x 4 (columns) of 128 x 64: 8 x 4 v_mfma_f32_16x16x32_f16
+// 8 waves as 2 (rows) x 4 (columns) of 128 x 64 (or 64 / 96 x 64 with the
+// smaller tiles): 8 x 4 v_mfma_f32_16x16x32_f16
 // tiles with fp32 accumulators; MFMA tile c of a wave reads positions
 // 16 c .. 16 c + 15 of its 64, i.e. columns 4 j + c, so every lane ends up with
 // 4 adjacent columns of each row it holds and stores them with one write.
@@ -39,17 +41,33 @@ namespace w4v {
 
 namespace {
 
-constexpr int BM = 256, BN = 256, BK = 32;
+constexpr int BN = 256, BK = 32;
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kGroupM = 8;                          // row blocks per raster group
-constexpr int kSlots = 5;                           // stages resident in LDS
-constexpr int kAhead = kSlots - 1;                  // stages requested ahead of the MFMAs
-constexpr uint32_t kA = 0, kW = 16384, kScale = 20480, kZero = 21504;   // offsets in a slot
-constexpr uint32_t kSlotBytes = 22528;
 constexpr uint32_t kBTile = 16384;                  // fp16 B tile: 256 columns x 32 k
-constexpr uint32_t kSink = kSlots * kSlotBytes + 2 * kBTile;   // 1 KiB for DMAs with no data
-constexpr uint32_t kLdsBytes = kSink + 1024;
+constexpr uint32_t kLdsLimit = 160 * 1024;          // LDS per block on gfx950
+
+// LDS layout for MTW m-tiles per wave (block tiles of 32 MTW rows): a slot
+// holds one stage's activation tile, packed words, scales and zero words; as
+// many slots as fit beside the two B tiles and the sink, so that smaller
+// tiles keep more stages in flight
+template <int MTW>
+struct Lds {
+  static constexpr uint32_t kA = 0;                          // 32 MTW rows x 64 bytes
+  static constexpr uint32_t kW = 2048u * MTW;                // 4 packed rows x 256 columns
+  static constexpr uint32_t kScale = kW + 4096;              // 256 fp16 scales
+  static constexpr uint32_t kZero = kScale + 1024;           // 32 zero words (1 KiB reserved)
+  static constexpr uint32_t kSlotBytes = kZero + 1024;
+  static constexpr int kSlots = (int)((kLdsLimit - 2 * kBTile - 1024) / kSlotBytes);
+  static constexpr int kAhead = kSlots - 1;                  // stages requested ahead of the MFMAs
+  static constexpr uint32_t kSink = kSlots * kSlotBytes + 2 * kBTile;   // DMAs with no data
+  static constexpr uint32_t kBytes = kSink + 1024;
+  static_assert(kBytes <= kLdsLimit, "LDS layout exceeds the block's LDS");
+};
+
+// s_waitcnt immediate that waits for vmcnt <= n and nothing else (gfx9 field layout)
+constexpr int vmcnt_only(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 constexpr uint32_t kNoMem = 0x80000000u;            // past every resource: reads no memory
 
 // packed word (8 consecutive k of one column) -> 8 fp16 s * (q - z) in natural
@@ -68,10 +86,19 @@ __device__ __forceinline__ u32x4 dequant_natural(uint32_t w, f16x2 z1024, f16x2 
   return u32x4{f(p0), f(p1), f(p2), f(p3)};
 }
 
-template <int Q>    // 1: group size 128, 4: group size 32
+// Q = 1: group size 128, 4: group size 32.  MTW 16-row m-tiles per wave: block
+// tiles of 32 MTW rows (256, or 192 / 128 for blocks of fewer rows, which then
+// spend no MFMAs and no activation reads on rows that do not exist).
+template <int Q, int MTW>
 __global__ __launch_bounds__(kThreads) void w4a16_mfma_kernel(GemmArgs a, int mblocks, int nblocks,
                                                               int S, float* partials) {
-  __shared__ __attribute__((aligned(1024))) unsigned char lds[kLdsBytes];
+  constexpr int BM = 32 * MTW;
+  using L = Lds<MTW>;
+  constexpr int kSlots = L::kSlots, kAhead = L::kAhead;
+  constexpr uint32_t kA = L::kA, kW = L::kW, kScale = L::kScale, kZero = L::kZero;
+  constexpr uint32_t kSlotBytes = L::kSlotBytes, kSink = L::kSink;
+  static_assert(3 * (kAhead - 1) <= 63, "vmcnt counts past its range");
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[L::kBytes];
   const int t = threadIdx.x;
   const int lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
@@ -104,9 +131,11 @@ __global__ __launch_bounds__(kThreads) void w4a16_mfma_kernel(GemmArgs a, int mb
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int r = wave * 32 + i * 16 + (lane >> 2);
-    const int m = m0 + r < M ? m0 + r : M - 1;      // rows past M: read a valid row, never stored
     const int chunk = (lane & 3) ^ lds_sw4(r);
-    xo[i] = ((uint32_t)m * (uint32_t)a.ldx + (uint32_t)chunk * 8) * 2;
+    // rows past M or past the tile: the DMA is issued (fixed counts) but reads
+    // nothing; those rows' results are never stored
+    xo[i] = r < BM && m0 + r < M ? ((uint32_t)(m0 + r) * (uint32_t)a.ldx + (uint32_t)chunk * 8) * 2
+                                 : kNoMem;
   }
   const uint32_t Nu = (uint32_t)N;
   u32x4s r3 = dma_rsrc(a.qweight);
@@ -135,9 +164,11 @@ __global__ __launch_bounds__(kThreads) void w4a16_mfma_kernel(GemmArgs a, int mb
   auto issue = [&](int s) {
     const bool live = s < s_hi;
     const uint32_t slot = lds0 + (uint32_t)((s - s_lo) % kSlots) * kSlotBytes;
-    const uint32_t base = slot + kA + (uint32_t)wave * 2048;
-    dma16(base, rx, live ? xo[0] + (uint32_t)s * BK * 2 : kNoMem);
-    dma16(base + 1024, rx, live ? xo[1] + (uint32_t)s * BK * 2 : kNoMem);
+    // waves whose rows lie past a smaller tile write their (empty) DMAs to the sink
+    const uint32_t base = wave * 32 < BM ? slot + kA + (uint32_t)wave * 2048 : lds0 + kSink;
+    const uint32_t base1 = wave * 32 < BM ? base + 1024 : lds0 + kSink;
+    dma16(base, rx, live ? xo[0] + (uint32_t)s * BK * 2 : kNoMem);      // kNoMem + s BK 2 stays
+    dma16(base1, rx, live ? xo[1] + (uint32_t)s * BK * 2 : kNoMem);     // past 2 GiB
     uint32_t o = o3;
     if (o != kNoMem)
       o += wave < 4 ? (uint32_t)s * step3 : (uint32_t)(s * BK / (128 / Q)) * gstep;
@@ -174,10 +205,10 @@ __global__ __launch_bounds__(kThreads) void w4a16_mfma_kernel(GemmArgs a, int mb
     *reinterpret_cast<u32x4*>(bt + bw1) = dequant_natural(d.w1, z1024, sc, magic);
   };
 
-  int ao[8], bo[4];                                 // MFMA operand offsets within a tile
+  int ao[MTW], bo[4];                               // MFMA operand offsets within a tile
 #pragma unroll
-  for (int mt = 0; mt < 8; ++mt) {
-    const int r = wm * 128 + mt * 16 + l16;
+  for (int mt = 0; mt < MTW; ++mt) {
+    const int r = wm * 16 * MTW + mt * 16 + l16;
     ao[mt] = (r * 4 + (kb ^ lds_sw4(r))) * 16;
   }
 #pragma unroll
@@ -185,15 +216,15 @@ __global__ __launch_bounds__(kThreads) void w4a16_mfma_kernel(GemmArgs a, int mb
     const int p = wn * 64 + c * 16 + l16;
     bo[c] = (p * 4 + (kb ^ lds_sw4(p))) * 16;
   }
-  auto read_a = [&](int s, f16x8 (&av)[8]) {
+  auto read_a = [&](int s, f16x8 (&av)[MTW]) {
     const unsigned char* as = lds + ((s - s_lo) % kSlots) * kSlotBytes + kA;
 #pragma unroll
-    for (int mt = 0; mt < 8; ++mt) av[mt] = *reinterpret_cast<const f16x8*>(as + ao[mt]);
+    for (int mt = 0; mt < MTW; ++mt) av[mt] = *reinterpret_cast<const f16x8*>(as + ao[mt]);
   };
 
-  f32x4 acc[8][4];
+  f32x4 acc[MTW][4];
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
+  for (int i = 0; i < MTW; ++i)
 #pragma unroll
     for (int c = 0; c < 4; ++c) acc[i][c] = f32x4{0.f, 0.f, 0.f, 0.f};
 
@@ -203,8 +234,9 @@ __global__ __launch_bounds__(kThreads) void w4a16_mfma_kernel(GemmArgs a, int mb
   //      landed for this wave (DMAs of the two stages after it may still be in
   //      flight); after the barrier it has for every wave, B(s) is complete and
   //      every wave is done with the slot and B tile of stage s - 1.
-  auto step = [&](int s, const f16x8 (&av)[8], f16x8 (&an)[8]) {
-    __builtin_amdgcn_s_waitcnt(0x0f76);             // vmcnt(6): two stages still in flight
+  auto step = [&](int s, const f16x8 (&av)[MTW], f16x8 (&an)[MTW]) {
+    // stages s + 2 .. s + kAhead - 1 still in flight, three DMAs each
+    __builtin_amdgcn_s_waitcnt(vmcnt_only(3 * (kAhead - 2)));
     lds_barrier();
     const unsigned char* bs = lds + kSlots * kSlotBytes + ((s - s_lo) & 1) * kBTile;
     f16x8 bv[4];
@@ -213,7 +245,7 @@ __global__ __launch_bounds__(kThreads) void w4a16_mfma_kernel(GemmArgs a, int mb
     const DqIn d = dq_read(s + 1);
     read_a(s + 1, an);
 #pragma unroll
-    for (int mt = 0; mt < 8; ++mt)
+    for (int mt = 0; mt < MTW; ++mt)
 #pragma unroll
       for (int c = 0; c < 4; ++c) acc[mt][c] = mfma16x16x32(av[mt], bv[c], acc[mt][c]);
     dq_write(s + 1, d);
@@ -224,7 +256,7 @@ __global__ __launch_bounds__(kThreads) void w4a16_mfma_kernel(GemmArgs a, int mb
     __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);      // B fragment reads
     __builtin_amdgcn_sched_group_barrier(0x100, 12, 0);     // dequant inputs, next A fragments
 #pragma unroll
-    for (int i = 0; i < 32; ++i) {
+    for (int i = 0; i < 4 * MTW; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);    // one MFMA
       __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);    // two VALU
     }
@@ -235,10 +267,10 @@ __global__ __launch_bounds__(kThreads) void w4a16_mfma_kernel(GemmArgs a, int mb
   //      stage and read its A fragments
 #pragma unroll
   for (int i = 0; i < kAhead; ++i) issue(s_lo + i);
-  __builtin_amdgcn_s_waitcnt(0x0f79);               // vmcnt(9): stage s_lo has landed
+  __builtin_amdgcn_s_waitcnt(vmcnt_only(3 * (kAhead - 1)));   // stage s_lo has landed
   lds_barrier();
   dq_write(s_lo, dq_read(s_lo));
-  f16x8 a0[8], a1[8];
+  f16x8 a0[MTW], a1[MTW];
   read_a(s_lo, a0);
 
   int s = s_lo;
@@ -254,10 +286,10 @@ __global__ __launch_bounds__(kThreads) void w4a16_mfma_kernel(GemmArgs a, int mb
   if (S > 1) {
     float* pp = partials + (size_t)split * M * N;
 #pragma unroll
-    for (int mt = 0; mt < 8; ++mt)
+    for (int mt = 0; mt < MTW; ++mt)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int m = m0 + wm * 128 + mt * 16 + 4 * kb + e;
+        const int m = m0 + wm * 16 * MTW + mt * 16 + 4 * kb + e;
         if (m < M) {
           const f32x4 val = {acc[mt][0][e], acc[mt][1][e], acc[mt][2][e], acc[mt][3][e]};
           *reinterpret_cast<f32x4*>(pp + (size_t)m * N + col) = val;
@@ -266,10 +298,10 @@ __global__ __launch_bounds__(kThreads) void w4a16_mfma_kernel(GemmArgs a, int mb
     return;
   }
 #pragma unroll
-  for (int mt = 0; mt < 8; ++mt)
+  for (int mt = 0; mt < MTW; ++mt)
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const int m = m0 + wm * 128 + mt * 16 + 4 * kb + e;
+      const int m = m0 + wm * 16 * MTW + mt * 16 + 4 * kb + e;
       if (m < M) {
         const f16x2 lo = {(_Float16)(a.alpha * acc[mt][0][e]), (_Float16)(a.alpha * acc[mt][1][e])};
         const f16x2 hi = {(_Float16)(a.alpha * acc[mt][2][e]), (_Float16)(a.alpha * acc[mt][3][e])};
@@ -296,10 +328,24 @@ __global__ __launch_bounds__(256) void w4a16_mfma_reduce_kernel(const float* __r
                                                      __builtin_bit_cast(uint32_t, hi)};
 }
 
+template <int MTW>
+void launch_m(const GemmArgs& a, const MfmaPlan& p, dim3 grid, float* partials,
+              hipStream_t stream) {
+  if (a.group_size == 32)
+    hipLaunchKernelGGL((w4a16_mfma_kernel<4, MTW>), grid, dim3(kThreads), 0, stream, a, p.mblocks,
+                       p.nblocks, p.splits, partials);
+  else
+    hipLaunchKernelGGL((w4a16_mfma_kernel<1, MTW>), grid, dim3(kThreads), 0, stream, a, p.mblocks,
+                       p.nblocks, p.splits, partials);
+}
+
 }  // namespace
 
 MfmaPlan plan_w4a16_mfma(int M, int N, int K, int num_cus) {
   MfmaPlan p{};
+  // block rows: 256, or the smallest of 128 / 192 that holds every row
+  p.mtw = M <= 128 ? 4 : (M <= 192 ? 6 : 8);
+  const int BM = 32 * p.mtw;
   p.mblocks = (M + BM - 1) / BM;
   p.nblocks = (N + BN - 1) / BN;
   const int tiles = p.mblocks * p.nblocks;
@@ -325,12 +371,10 @@ MfmaPlan plan_w4a16_mfma(int M, int N, int K, int num_cus) {
 hipError_t launch_w4a16_mfma(const GemmArgs& a, const MfmaPlan& p, float* partials,
                              hipStream_t stream) {
   const dim3 grid(p.mblocks * p.nblocks, p.splits);
-  if (a.group_size == 32)
-    hipLaunchKernelGGL(w4a16_mfma_kernel<4>, grid, dim3(kThreads), 0, stream, a, p.mblocks,
-                       p.nblocks, p.splits, partials);
-  else
-    hipLaunchKernelGGL(w4a16_mfma_kernel<1>, grid, dim3(kThreads), 0, stream, a, p.mblocks,
-                       p.nblocks, p.splits, partials);
+  if (p.mtw == 8) launch_m<8>(a, p, grid, partials, stream);
+  else if (p.mtw == 6) launch_m<6>(a, p, grid, partials, stream);
+  else if (p.mtw == 4) launch_m<4>(a, p, grid, partials, stream);
+  else return hipErrorInvalidValue;
   if (p.splits > 1) {
     const size_t quads = ((size_t)a.M * a.N + 3) / 4;
     hipLaunchKernelGGL(w4a16_mfma_reduce_kernel, dim3((unsigned)((quads + 255) / 256)), dim3(256),

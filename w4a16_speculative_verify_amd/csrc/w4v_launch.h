@@ -62,7 +62,8 @@ hipError_t launch_w4a16_skinny(const GemmArgs& a, const GemmPlan& p, void* works
 // workspace for shapes with few tiles
 constexpr int kMfmaMinRows = 33;
 struct MfmaPlan {
-  int mblocks, nblocks;  // 256 x 256 block tiles
+  int mtw;               // 16-row m-tiles per wave: block tiles of 32 mtw rows x 256 columns
+  int mblocks, nblocks;
   int splits;            // K-splits (1 = none)
   size_t partial_bytes;  // fp32 [splits][M][N] when splits > 1
 };
