@@ -9,8 +9,8 @@
 // LDS DMA (buffer_load ... lds: no registers; issued from inline assembly so
 // that the compiler does not wait for it at unrelated LDS accesses -- the
 // kernel waits itself with explicit vmcnt counts), kSlots stages deep in a
-// ring of LDS slots (5, or 7 / 9 with the smaller tiles), so that a stage's data has several stages of MFMA time to
-// arrive.  A slot holds one stage's
+// ring of LDS slots (5, or 7 / 9 with the smaller tiles), so that a stage's
+// data has several stages of MFMA time to arrive.  A slot holds one stage's
 //   A     the tile's rows x 32 k fp16, row r's 16-byte chunk c stored at
 //         r * 4 + (c ^ lds_sw4(r));
 //   W     the packed words, 4 packed rows x 256 columns;
