@@ -146,6 +146,47 @@ def counter_traffic():
     return rec["traffic_bytes_per_launch"] if h.hexdigest() == rec["sha256"] else None
 
 
+def device_info(dev):
+    """Name, compute units and clocks of the device the numbers come from (torch's
+    properties, and the HIP runtime's attributes for the clocks)."""
+    import ctypes
+    import torch
+    p = torch.cuda.get_device_properties(dev)
+    info = {"name": p.name, "arch": getattr(p, "gcnArchName", ""), "cus": p.multi_processor_count,
+            "hbm_gib": round(p.total_memory / 2**30, 1)}
+    try:
+        hip = ctypes.CDLL("libamdhip64.so")
+        val = ctypes.c_int(0)
+        # hipDeviceAttributeClockRate = 5, hipDeviceAttributeMemoryClockRate = 60 (kHz)
+        for key, attr in (("clock_mhz", 5), ("mem_clock_mhz", 60)):
+            if hip.hipDeviceGetAttribute(ctypes.byref(val), attr, dev.index or 0) == 0:
+                info[key] = val.value // 1000
+    except OSError:
+        pass
+    return info
+
+
+def read_probe(dev, mib: int = 1024, reps: int = 10):
+    """The HBM read rate the device reaches: w4v_read_probe over a buffer four
+    times the last-level cache, averaged over ``reps`` back-to-back calls."""
+    import torch
+
+    import w4a16_speculative_verify_amd as w4v
+    src = torch.ones(mib << 18, dtype=torch.int32, device=dev)
+    out = w4v.read_probe(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        w4v.read_probe(src, out=out)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / reps
+    nbytes = src.numel() * 4
+    del src, out
+    return {"bytes": nbytes, "us": round(us, 2), "gbs": round(nbytes / (us * 1e-6) / 1e9, 1)}
+
+
 def prefill(dev, reps: int = 10):
     """The prefill-shaped linears (gate+up 2560->19456, down 9728->2560) at
     M = 2048 and 8192 through w4a16_gemm (from 33 rows on: the LDS-tiled MFMA
@@ -176,9 +217,22 @@ def prefill(dev, reps: int = 10):
             torch.cuda.synchronize()
             us = e0.elapsed_time(e1) * 1e3 / reps
             tf = 2.0 * m * k * n / (us * 1e-6) / 1e12
+            # yardstick only: the vendor fp16 GEMM on fp16 weights of the same shape
+            w16 = torch.randn((k, n), dtype=torch.float16, device=dev) * 0.02
+            torch.matmul(x, w16)
+            torch.cuda.synchronize()
+            e0.record()
+            for _ in range(reps):
+                torch.matmul(x, w16)
+            e1.record()
+            torch.cuda.synchronize()
+            us_ref = e0.elapsed_time(e1) * 1e3 / reps
             out[f"m{m}_{k}x{n}"] = {"us": round(us, 2), "tflops": round(tf, 1),
-                                    "frac_of_fp16_mfma_peak": round(tf / MFMA_FP16_PEAK_TFLOPS, 4)}
-            del x, y
+                                    "frac_of_fp16_mfma_peak": round(tf / MFMA_FP16_PEAK_TFLOPS, 4),
+                                    "torch_matmul_fp16_us": round(us_ref, 2),
+                                    "torch_matmul_fp16_tflops":
+                                        round(2.0 * m * k * n / (us_ref * 1e-6) / 1e12, 1)}
+            del x, y, w16
     return out
 
 
@@ -831,6 +885,9 @@ def main():
         print("[bench] timing the prompt-lookup drafter", file=sys.stderr, flush=True)
         draft = drafter(dev)
 
+    print("[bench] probing the HBM read rate", file=sys.stderr, flush=True)
+    probe = read_probe(dev)
+
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
@@ -860,6 +917,8 @@ def main():
         "mean_accepted_plus_one": round(tokens / args.steps, 3),
         "gemm_gbs": round(gemm_gbs, 1),
         "gemm_pct_of_hbm_peak": round(100 * gemm_gbs / HBM_PEAK_GBS, 2),
+        "hbm_read_probe": probe,
+        "gemm_pct_of_probed_read": round(100 * gemm_gbs / probe["gbs"], 2),
         "linears_us_per_step": round(lin_ms * 1e3, 2),
         "step_bytes": lin_b + lm_b,
         "wall_s_timed": round(wall, 4),
@@ -870,6 +929,7 @@ def main():
                      "bytes_per_launch": round(lin_b / n_launch),
                      "avg_launch_us": round(act_launch_us, 3)},
         "cpu_baseline": cpu,
+        "device": device_info(dev),
         "block_linear_c1": c1,
         "linears_one_launch_chain": chain,
         "prefill": pre,

@@ -56,6 +56,21 @@ const char* w4v_status_string(int status);
 int w4v_abi_version(void);
 
 /* ------------------------------------------------------------------------
+ * HBM read-bandwidth probe (a measurement helper, not a step of the verify
+ * path; the measurement method of the hot path asks for the read bandwidth
+ * the device actually reaches, reported beside the 8 TB/s peak).
+ * Reads `bytes` of device memory at `src` once (16-byte non-temporal loads)
+ * and writes one 32-bit XOR per block of what it read to `out`, so that the
+ * loads are not dropped; timing the call gives the read rate.
+ *   src    device, 16-byte aligned; bytes > 0, a multiple of 16.
+ *   out    device, w4v_read_probe_blocks() words, caller-owned.
+ * Enqueued on `stream`; returns W4V_ERR_INVALID_ARG (null, bad size),
+ * W4V_ERR_ALIGNMENT or W4V_ERR_HIP.
+ */
+int w4v_read_probe_blocks(void);
+int w4v_read_probe(const void* src, size_t bytes, uint32_t* out, void* stream);
+
+/* ------------------------------------------------------------------------
  * W4A16 linear (section 3: 4-bit weights, group size 128, 16-bit activations;
  * section 5: group size 32 for team #5's compressed-tensors target)
  *

@@ -42,6 +42,15 @@ def test_every_declared_symbol_is_exported(lib):
         assert getattr(lib, n) is not None
 
 
+def test_read_probe_validation(lib):
+    assert lib.w4v_read_probe_blocks() > 0
+    assert lib.w4v_read_probe(None, 1024, A, None) == INVALID
+    assert lib.w4v_read_probe(A, 0, A, None) == INVALID
+    assert lib.w4v_read_probe(A, 1000, A, None) == INVALID      # not a multiple of 16
+    assert lib.w4v_read_probe(A + 8, 1024, A, None) == ALIGN
+    assert lib.w4v_read_probe(A, 1024, None, None) == INVALID
+
+
 def test_version_and_status_strings(lib):
     assert w4v.abi_version() == 1
     for st in (OK, INVALID, UNSUPPORTED, ALIGN, WORKSPACE, -5):

@@ -37,6 +37,8 @@ _sz = ctypes.c_size_t
 SIGNATURES = {
     "w4v_status_string": (ctypes.c_char_p, [_int]),
     "w4v_abi_version": (_int, []),
+    "w4v_read_probe_blocks": (_int, []),
+    "w4v_read_probe": (_int, [_vp, _sz, _vp, _vp]),
     "w4a16_gemm_workspace_size": (_sz, [_int, _int, _int, _int]),
     "w4a16_gemm": (_int, [_vp, _i64, _vp, _vp, _vp, _vp, _i64, _int, _int, _int, _int,
                           ctypes.c_float, _vp, _sz, _vp]),
@@ -240,6 +242,21 @@ def w8a16_lmhead_argmax(h, w, scales, target_ids=None, max_logits=None, want_max
                                     _ptr(workspace), wbytes, _stream(stream))
     _check(st, "w8a16_lmhead_argmax")
     return target_ids, max_logits
+
+
+def read_probe(src, out=None, stream=None):
+    """Read every byte of the device tensor src once (the HBM read-bandwidth probe);
+    returns out, int32 [w4v_read_probe_blocks()], one XOR word per block."""
+    import torch
+    if src.device.type != "cuda" or not src.is_contiguous():
+        raise ValueError("src must be a contiguous device tensor")
+    nb = load().w4v_read_probe_blocks()
+    if out is None:
+        out = torch.empty(nb, dtype=torch.int32, device=src.device)
+    st = load().w4v_read_probe(_ptr(src), src.numel() * src.element_size(), _ptr(out),
+                               _stream(stream))
+    _check(st, "w4v_read_probe")
+    return out
 
 
 def greedy_verify(target_ids, draft_ids, vocab: int, accepted_len=None, out_tokens=None,

@@ -14,7 +14,8 @@ OBJDIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libw4v.so")
 
 SOURCES = ["w4a16_skinny.hip", "w4a16_mfma.hip", "w4a16_chain.hip",
-           "w8a16_lmhead.hip", "greedy_verify.hip", "ngram_draft.hip", "gdn_commit.hip", "lib_gemm.cpp", "api.cpp"]
+           "w8a16_lmhead.hip", "greedy_verify.hip", "ngram_draft.hip", "gdn_commit.hip", "read_probe.hip", "lib_gemm.cpp",
+           "api.cpp"]
 # the vendor GEMM library behind the fp16 linear (f16_gemm) only
 LIBS = ["-L/opt/rocm/lib", "-lhipblaslt", "-Wl,-rpath,/opt/rocm/lib"]
 

@@ -447,6 +447,15 @@ int w8a16_lmhead_argmax(const void* h, int64_t ldh, const int8_t* w, const void*
                     nullptr, workspace, workspace_bytes, stream);
 }
 
+int w4v_read_probe_blocks(void) { return w4v::kReadProbeBlocks; }
+
+int w4v_read_probe(const void* src, size_t bytes, uint32_t* out, void* stream) {
+  if (!src || !out || bytes == 0 || bytes % 16 != 0) return W4V_ERR_INVALID_ARG;
+  if (!aligned(src, 16) || !aligned(out, 4)) return W4V_ERR_ALIGNMENT;
+  hipError_t e = w4v::launch_read_probe(src, bytes, out, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? W4V_OK : W4V_ERR_HIP;
+}
+
 int greedy_verify(const int32_t* target_ids, const int32_t* draft_ids, int B, int K, int V,
                   int32_t* accepted_len, int32_t* out_tokens, void* stream) {
   if (B < 0 || K < 0 || V <= 0) return W4V_ERR_INVALID_ARG;

@@ -207,6 +207,10 @@ hipError_t launch_gdn_commit(float* state, const float* k, const float* v, const
                              int D, hipStream_t stream);
 
 // ---------------------------------------------------------------- verify
+// HBM read-bandwidth probe: kReadProbeBlocks blocks, one XOR word each in out
+constexpr int kReadProbeBlocks = 2048;
+hipError_t launch_read_probe(const void* src, size_t bytes, uint32_t* out, hipStream_t stream);
+
 hipError_t launch_greedy_verify(const int32_t* target_ids, const int32_t* draft_ids, int B, int K,
                                 int V, int32_t* accepted_len, int32_t* out_tokens,
                                 hipStream_t stream);
