@@ -463,11 +463,18 @@ void launch_t(const GemmArgs& a, const GemmPlan& p, unsigned* tickets, float* pa
                      G / p.splits, G % p.splits, a, tickets, partials);
 }
 
-// Four k-slices per block, one or two tiles, three steps in flight per wave;
-// one batch of partial loads up to 8 splits, batches of 16 beyond.
+// Four k-slices per block (two for 16-row two-tile blocks), one or two tiles,
+// three steps in flight per wave; one batch of partial loads up to 8 splits,
+// batches of 16 beyond.
 template <int MT, int WT, int Q, int DX>
 void launch_w(const GemmArgs& a, const GemmPlan& p, unsigned* tickets, float* partials,
               hipStream_t stream) {
+  if constexpr (MT == 1 && WT == 2) {
+    if (p.wk == 2) {
+      launch_t<MT, WT, 2, 3, 8, Q, DX>(a, p, tickets, partials, stream);
+      return;
+    }
+  }
   if (p.splits <= 8) launch_t<MT, WT, 4, 3, 8, Q, DX>(a, p, tickets, partials, stream);
   else launch_t<MT, WT, 4, 3, 16, Q, DX>(a, p, tickets, partials, stream);
 }
@@ -535,6 +542,11 @@ GemmPlan plan_w4a16(int M, int N, int K, int num_cus) {
       }
     }
   }
+  // 16-row blocks of two tiles (tiles outnumbering the CUs, unsplit): two
+  // k-slices of ten groups per wave instead of four of five (gate+up at
+  // M = 16 on MI355X: 10.96 against 11.15 us; one k-slice 15.4 us, one tile
+  // per block with two k-slices 13.8 us)
+  if (p.mt == 1 && p.wt == 2 && splits == 1) p.wk = 2;
   p.col_blocks = (p.tiles + p.wt - 1) / p.wt;
   p.splits = splits;
   p.depth = 3;
@@ -584,7 +596,8 @@ hipError_t launch_w4a16_skinny(const GemmArgs& a, const GemmPlan& p, void* works
     tickets = static_cast<unsigned*>(workspace);
     partials = reinterpret_cast<float*>(static_cast<char*>(workspace) + p.ticket_bytes);
   }
-  if ((p.wt != 1 && p.wt != 2) || p.wk != 4 || p.depth != 3 ||
+  if ((p.wt != 1 && p.wt != 2) ||
+      (p.wk != 4 && !(p.wk == 2 && p.mt == 1 && p.wt == 2 && p.splits == 1)) || p.depth != 3 ||
       (a.group_size != 128 && a.group_size != 32))
     return hipErrorInvalidValue;
   const bool g32 = a.group_size == 32;
