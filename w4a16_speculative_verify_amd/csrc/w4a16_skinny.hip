@@ -156,6 +156,7 @@ __global__ __launch_bounds__(64 * WT * WK) void w4a16_skinny_kernel(
     int pM, int pldx, int splits, int gbase, int grem, GemmArgs a, unsigned* tickets,
     float* partials) {
   static_assert(!DX || (MT == 1 && WT == 1), "direct fragments: one row tile, one tile");
+  static_assert(D == 2 || D == 3, "the step loop unrolls rings of two or three groups");
   constexpr int NW = WT * WK;                       // waves per block
   constexpr int kXWords = MT * 16 * kXRowWords;     // one group's activation tile
   const int lane = threadIdx.x & 63;
@@ -471,7 +472,7 @@ void launch_w(const GemmArgs& a, const GemmPlan& p, unsigned* tickets, float* pa
               hipStream_t stream) {
   if constexpr (MT == 1 && WT == 2) {
     if (p.wk == 2) {
-      launch_t<MT, WT, 2, 3, 8, Q, DX>(a, p, tickets, partials, stream);
+      launch_t<MT, WT, 2, 2, 8, Q, DX>(a, p, tickets, partials, stream);
       return;
     }
   }
@@ -542,14 +543,18 @@ GemmPlan plan_w4a16(int M, int N, int K, int num_cus) {
       }
     }
   }
+  p.depth = 3;
   // 16-row blocks of two tiles (tiles outnumbering the CUs, unsplit): two
-  // k-slices of ten groups per wave instead of four of five (gate+up at
-  // M = 16 on MI355X: 10.96 against 11.15 us; one k-slice 15.4 us, one tile
-  // per block with two k-slices 13.8 us)
-  if (p.mt == 1 && p.wt == 2 && splits == 1) p.wk = 2;
+  // k-slices of ten groups per wave instead of four of five, two groups in
+  // flight per wave (gate+up at M = 16 on MI355X: 10.96 against 11.15 us with
+  // three in flight, 10.9 with two; one k-slice 15.4 us, one tile per block
+  // with two k-slices 13.8 us)
+  if (p.mt == 1 && p.wt == 2 && splits == 1) {
+    p.wk = 2;
+    p.depth = 2;
+  }
   p.col_blocks = (p.tiles + p.wt - 1) / p.wt;
   p.splits = splits;
-  p.depth = 3;
   if (splits > 1) {
     p.ticket_bytes = kTicketRegion;
     p.partial_bytes = (size_t)p.mblocks * rows_blk * p.col_blocks * p.wt * kColTile *
@@ -596,8 +601,8 @@ hipError_t launch_w4a16_skinny(const GemmArgs& a, const GemmPlan& p, void* works
     tickets = static_cast<unsigned*>(workspace);
     partials = reinterpret_cast<float*>(static_cast<char*>(workspace) + p.ticket_bytes);
   }
-  if ((p.wt != 1 && p.wt != 2) ||
-      (p.wk != 4 && !(p.wk == 2 && p.mt == 1 && p.wt == 2 && p.splits == 1)) || p.depth != 3 ||
+  const bool two_slices = p.wk == 2 && p.depth == 2 && p.mt == 1 && p.wt == 2 && p.splits == 1;
+  if ((p.wt != 1 && p.wt != 2) || ((p.wk != 4 || p.depth != 3) && !two_slices) ||
       (a.group_size != 128 && a.group_size != 32))
     return hipErrorInvalidValue;
   const bool g32 = a.group_size == 32;

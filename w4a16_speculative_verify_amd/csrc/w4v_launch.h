@@ -44,10 +44,10 @@ struct GemmPlan {
   int mblocks;       // blocks along M, each 16*mt rows
   int tiles;         // ceil(N / 64)
   int wt;            // 64-column tiles per block (1 or 2)
-  int wk;            // k-slices per block (4)
+  int wk;            // k-slices per block (4; 2 for 16-row two-tile blocks)
   int col_blocks;    // ceil(tiles / wt)
   int splits;        // split-K factor across blocks (1 = none)
-  int depth;         // groups in flight per wave (3)
+  int depth;         // groups in flight per wave (3; 2 with two k-slices)
   size_t ticket_bytes;
   size_t partial_bytes;
   size_t workspace_bytes() const { return ticket_bytes + partial_bytes; }
