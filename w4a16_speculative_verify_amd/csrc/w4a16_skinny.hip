@@ -465,7 +465,7 @@ void launch_t(const GemmArgs& a, const GemmPlan& p, unsigned* tickets, float* pa
 }
 
 // Four k-slices per block (two for 16-row two-tile blocks), one or two tiles,
-// three steps in flight per wave; one batch of partial loads up to 8 splits,
+// two groups in flight per wave; one batch of partial loads up to 8 splits,
 // batches of 16 beyond.
 template <int MT, int WT, int Q, int DX>
 void launch_w(const GemmArgs& a, const GemmPlan& p, unsigned* tickets, float* partials,
@@ -476,8 +476,8 @@ void launch_w(const GemmArgs& a, const GemmPlan& p, unsigned* tickets, float* pa
       return;
     }
   }
-  if (p.splits <= 8) launch_t<MT, WT, 4, 3, 8, Q, DX>(a, p, tickets, partials, stream);
-  else launch_t<MT, WT, 4, 3, 16, Q, DX>(a, p, tickets, partials, stream);
+  if (p.splits <= 8) launch_t<MT, WT, 4, 2, 8, Q, DX>(a, p, tickets, partials, stream);
+  else launch_t<MT, WT, 4, 2, 16, Q, DX>(a, p, tickets, partials, stream);
 }
 
 // a single activation row on one-tile blocks takes its A fragments directly
@@ -543,16 +543,15 @@ GemmPlan plan_w4a16(int M, int N, int K, int num_cus) {
       }
     }
   }
-  p.depth = 3;
+  // two groups in flight per wave: against three, on MI355X at M = 16 per
+  // launch QKV 6.77 -> 6.10 us, O 6.03 -> 5.69, down 8.07 -> 7.34, and the
+  // 144 linears at M = 1 1,061 -> 1,012 us (a deeper ring was slower still)
+  p.depth = 2;
   // 16-row blocks of two tiles (tiles outnumbering the CUs, unsplit): two
-  // k-slices of ten groups per wave instead of four of five, two groups in
-  // flight per wave (gate+up at M = 16 on MI355X: 10.96 against 11.15 us with
-  // three in flight, 10.9 with two; one k-slice 15.4 us, one tile per block
+  // k-slices of ten groups per wave instead of four of five (gate+up at
+  // M = 16: 10.85 against 11.15 us; one k-slice 15.4 us, one tile per block
   // with two k-slices 13.8 us)
-  if (p.mt == 1 && p.wt == 2 && splits == 1) {
-    p.wk = 2;
-    p.depth = 2;
-  }
+  if (p.mt == 1 && p.wt == 2 && splits == 1) p.wk = 2;
   p.col_blocks = (p.tiles + p.wt - 1) / p.wt;
   p.splits = splits;
   if (splits > 1) {
@@ -601,8 +600,8 @@ hipError_t launch_w4a16_skinny(const GemmArgs& a, const GemmPlan& p, void* works
     tickets = static_cast<unsigned*>(workspace);
     partials = reinterpret_cast<float*>(static_cast<char*>(workspace) + p.ticket_bytes);
   }
-  const bool two_slices = p.wk == 2 && p.depth == 2 && p.mt == 1 && p.wt == 2 && p.splits == 1;
-  if ((p.wt != 1 && p.wt != 2) || ((p.wk != 4 || p.depth != 3) && !two_slices) ||
+  const bool two_slices = p.wk == 2 && p.mt == 1 && p.wt == 2 && p.splits == 1;
+  if ((p.wt != 1 && p.wt != 2) || (p.wk != 4 && !two_slices) || p.depth != 2 ||
       (a.group_size != 128 && a.group_size != 32))
     return hipErrorInvalidValue;
   const bool g32 = a.group_size == 32;

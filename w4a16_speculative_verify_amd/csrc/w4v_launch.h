@@ -47,7 +47,7 @@ struct GemmPlan {
   int wk;            // k-slices per block (4; 2 for 16-row two-tile blocks)
   int col_blocks;    // ceil(tiles / wt)
   int splits;        // split-K factor across blocks (1 = none)
-  int depth;         // groups in flight per wave (3; 2 with two k-slices)
+  int depth;         // groups in flight per wave (2)
   size_t ticket_bytes;
   size_t partial_bytes;
   size_t workspace_bytes() const { return ticket_bytes + partial_bytes; }
