@@ -464,18 +464,11 @@ void launch_t(const GemmArgs& a, const GemmPlan& p, unsigned* tickets, float* pa
                      G / p.splits, G % p.splits, a, tickets, partials);
 }
 
-// Four k-slices per block (two for 16-row two-tile blocks), one or two tiles,
-// two groups in flight per wave; one batch of partial loads up to 8 splits,
-// batches of 16 beyond.
+// Four k-slices per block, one or two tiles, two groups in flight per wave;
+// one batch of partial loads up to 8 splits, batches of 16 beyond.
 template <int MT, int WT, int Q, int DX>
 void launch_w(const GemmArgs& a, const GemmPlan& p, unsigned* tickets, float* partials,
               hipStream_t stream) {
-  if constexpr (MT == 1 && WT == 2) {
-    if (p.wk == 2) {
-      launch_t<MT, WT, 2, 2, 8, Q, DX>(a, p, tickets, partials, stream);
-      return;
-    }
-  }
   if (p.splits <= 8) launch_t<MT, WT, 4, 2, 8, Q, DX>(a, p, tickets, partials, stream);
   else launch_t<MT, WT, 4, 2, 16, Q, DX>(a, p, tickets, partials, stream);
 }
@@ -544,14 +537,11 @@ GemmPlan plan_w4a16(int M, int N, int K, int num_cus) {
     }
   }
   // two groups in flight per wave: against three, on MI355X at M = 16 per
-  // launch QKV 6.77 -> 6.10 us, O 6.03 -> 5.69, down 8.07 -> 7.34, and the
-  // 144 linears at M = 1 1,061 -> 1,012 us (a deeper ring was slower still)
+  // launch QKV 6.77 -> 6.10 us, O 6.03 -> 5.69, down 8.07 -> 7.34, gate+up
+  // 11.15 -> 10.65, and the 144 linears at M = 1 1,061 -> 1,012 us (deeper
+  // rings were slower still; two k-slices per block instead of four were
+  // slower at every shape with two groups in flight)
   p.depth = 2;
-  // 16-row blocks of two tiles (tiles outnumbering the CUs, unsplit): two
-  // k-slices of ten groups per wave instead of four of five (gate+up at
-  // M = 16: 10.85 against 11.15 us; one k-slice 15.4 us, one tile per block
-  // with two k-slices 13.8 us)
-  if (p.mt == 1 && p.wt == 2 && splits == 1) p.wk = 2;
   p.col_blocks = (p.tiles + p.wt - 1) / p.wt;
   p.splits = splits;
   if (splits > 1) {
@@ -600,8 +590,7 @@ hipError_t launch_w4a16_skinny(const GemmArgs& a, const GemmPlan& p, void* works
     tickets = static_cast<unsigned*>(workspace);
     partials = reinterpret_cast<float*>(static_cast<char*>(workspace) + p.ticket_bytes);
   }
-  const bool two_slices = p.wk == 2 && p.mt == 1 && p.wt == 2 && p.splits == 1;
-  if ((p.wt != 1 && p.wt != 2) || (p.wk != 4 && !two_slices) || p.depth != 2 ||
+  if ((p.wt != 1 && p.wt != 2) || p.wk != 4 || p.depth != 2 ||
       (a.group_size != 128 && a.group_size != 32))
     return hipErrorInvalidValue;
   const bool g32 = a.group_size == 32;

@@ -44,7 +44,7 @@ struct GemmPlan {
   int mblocks;       // blocks along M, each 16*mt rows
   int tiles;         // ceil(N / 64)
   int wt;            // 64-column tiles per block (1 or 2)
-  int wk;            // k-slices per block (4; 2 for 16-row two-tile blocks)
+  int wk;            // k-slices per block (4)
   int col_blocks;    // ceil(tiles / wt)
   int splits;        // split-K factor across blocks (1 = none)
   int depth;         // groups in flight per wave (2)
