@@ -426,7 +426,8 @@ def padded_batch(lins, lm_w, lm_s, steps: int = 50, warmup: int = 5):
     verify.  Weights: the first layer and the lm_head of the verify-step workload
     (same shapes and distributions); activations and drafts: the padded
     configuration's own seeded streams.  The linears at M = 168 run on the
-    LDS-tiled MFMA kernel."""
+    LDS-tiled MFMA kernel.  The timed steps run from one HIP graph, each step
+    reading its own drafts and writing its own accepted lengths."""
     import numpy as np
     import torch
     import gen
@@ -446,32 +447,29 @@ def padded_batch(lins, lm_w, lm_s, steps: int = 50, warmup: int = 5):
     for i in range(total):
         d_all[i], planned[i] = gen.make_drafts(drng, cfg, t_host)
     d_dev = torch.from_numpy(d_all).to(dev)
-    d_buf = torch.empty((cfg.batch, cfg.k_draft), dtype=torch.int32, device=dev)
     acc = torch.zeros((total, cfg.batch), dtype=torch.int32, device=dev)
+    # step i reads its own drafts (resident in HBM, as a drafter on the device
+    # leaves them) and writes its accepted lengths to its own row
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
-        st(x, d_buf)
+        for i in range(warmup):
+            st(x, d_dev[i], accepted_len=acc[i])
     torch.cuda.current_stream().wait_stream(s)
     torch.cuda.synchronize()
-    g_step, g_lin = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g_step):
-        st(x, d_buf)
+    # the timed steps in one graph, so that the host's per-replay cost is not timed
+    g_steps, g_lin = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g_steps):
+        for i in range(warmup, total):
+            st(x, d_dev[i], accepted_len=acc[i])
     with torch.cuda.graph(g_lin):
         st.linears_only(x)
-
-    def one(i):
-        d_buf.copy_(d_dev[i], non_blocking=True)
-        g_step.replay()
-        acc[i].copy_(st.accepted_len, non_blocking=True)
-
-    for i in range(warmup):
-        one(i)
+    g_steps.replay()
     torch.cuda.synchronize()
+    acc[warmup:].zero_()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
-    for i in range(warmup, total):
-        one(i)
+    g_steps.replay()
     e1.record()
     torch.cuda.synchronize()
     step_us = e0.elapsed_time(e1) * 1e3 / steps
@@ -512,7 +510,7 @@ def c1_row(dev, reps: int = 10):
     Each kernel's GB/s is taken over >= 1 GB of distinct weight copies launched
     back to back from a HIP graph (every launch reads its weights from HBM: no
     copy is reused within the 256 MB last-level cache); the whole step is timed
-    as 200 consecutive steps with fresh drafts captured in one HIP graph."""
+    as 200 consecutive steps, each with its own drafts, captured in one HIP graph."""
     import numpy as np
     import torch
 
@@ -592,15 +590,14 @@ def c1_row(dev, reps: int = 10):
         st(x, d_buf)
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
-    # all the steps in one graph (each: its drafts copied in, the step, its
-    # accepted length copied out), so that the host's per-replay launch cost,
-    # larger than this step, does not set the time
+    # all the steps in one graph (each reads its own drafts, resident in HBM as a
+    # drafter running on the device would leave them, and writes its accepted
+    # length to its own slot), so that the host's per-replay launch cost, larger
+    # than this step, does not set the time
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         for i in range(steps):
-            d_buf.copy_(d_dev[i], non_blocking=True)
-            st(x, d_buf)
-            acc[i:i + 1].copy_(st.accepted_len, non_blocking=True)
+            st(x, d_dev[i], accepted_len=acc[i:i + 1])
     g.replay()
     torch.cuda.synchronize()
     acc.zero_()

@@ -86,18 +86,20 @@ class VerifyStep:
             h = y
         return h
 
-    def head(self, h: torch.Tensor, drafts: torch.Tensor):
+    def head(self, h: torch.Tensor, drafts: torch.Tensor, accepted_len=None, out_tokens=None):
         """Fused lm_head + argmax + greedy verify on the final hidden rows (an fp16 lm_head
-        when no scales are given)."""
+        when no scales are given).  accepted_len / out_tokens: caller buffers for the
+        verify's outputs (int32 [batch] / [batch, K+1]); the step's own by default."""
+        acc = self.accepted_len if accepted_len is None else accepted_len
+        out = self.out_tokens if out_tokens is None else out_tokens
         if self.lm_s is None:
             return f16_lmhead_argmax_verify(h, self.lm_w, drafts, target_ids=self.target_ids,
-                                            max_logits=self.max_logits,
-                                            accepted_len=self.accepted_len,
-                                            out_tokens=self.out_tokens, workspace=self.workspace)
+                                            max_logits=self.max_logits, accepted_len=acc,
+                                            out_tokens=out, workspace=self.workspace)
         return w8a16_lmhead_argmax_verify(h, self.lm_w, self.lm_s, drafts,
                                           target_ids=self.target_ids, max_logits=self.max_logits,
-                                          accepted_len=self.accepted_len,
-                                          out_tokens=self.out_tokens, workspace=self.workspace)
+                                          accepted_len=acc, out_tokens=out,
+                                          workspace=self.workspace)
 
-    def __call__(self, x: torch.Tensor, drafts: torch.Tensor):
-        return self.head(self.linears_only(x), drafts)
+    def __call__(self, x: torch.Tensor, drafts: torch.Tensor, accepted_len=None, out_tokens=None):
+        return self.head(self.linears_only(x), drafts, accepted_len, out_tokens)
