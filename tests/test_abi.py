@@ -107,13 +107,19 @@ def test_gemm_workspace(lib):
     assert gemm(lib, K=4096, ldx=4096, g=32, ws=None, wsb=0) == WORKSPACE
     # sizes are a function of the shape alone
     assert w4v.gemm_workspace_size(16, 2560, 4096) == need
-    # from 33 rows on: the LDS-tiled MFMA kernel; a plan with K-splits keeps its fp32
-    # partials [S][M][N] after the skinny kernel's regions and needs that workspace (none,
-    # or a smaller one, is an error), an unsplit plan needs none
+    # from 33 rows on: the LDS-tiled MFMA kernel; a plan with K-splits keeps the fp32
+    # partials of its split tiles, [S][tiles][rows x 256] (128-row tiles up to 128 rows),
+    # after the skinny kernel's regions and needs that workspace (none, or a smaller one,
+    # is an error); an unsplit plan needs none
     big = w4v.gemm_workspace_size(33, 2560, 4096)
     rest = big - (64 << 10) - (4 << 20)
-    assert rest > 0 and rest % (33 * 2560 * 4) == 0 and rest // (33 * 2560 * 4) > 1
-    assert w4v.gemm_workspace_size(8192, 2560, 4096) == 0      # 320 block tiles: no split
+    tile = 128 * 256 * 4
+    assert rest > 0 and rest % (10 * tile) == 0 and rest // (10 * tile) > 1
+    # 256 full-size tiles (one round on 256 CUs): whole tiles, no partials
+    assert w4v.gemm_workspace_size(8192, 2048, 4096) == 0
+    # 320 tiles: 256 whole, the 64 of the partial second round split over the idle CUs
+    tail = w4v.gemm_workspace_size(8192, 2560, 4096) - (64 << 10) - (4 << 20)
+    assert tail > 0 and tail % (64 * 256 * 256 * 4) == 0
     assert w4v.gemm_workspace_size(33, 2560, 4096, 32) == big   # group size 32: same plan
     assert gemm(lib, M=33, K=4096, ldx=4096, ws=A * 256, wsb=big - 1) == WORKSPACE
     assert gemm(lib, M=33, K=4096, ldx=4096, ws=None, wsb=0) == WORKSPACE

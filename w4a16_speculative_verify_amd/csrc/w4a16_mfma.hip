@@ -31,9 +31,11 @@
 // dequantisation between them, then the stage kSlots - 1 ahead is requested.
 // Blocks are ordered in groups of 8 row blocks, so that the blocks running
 // together share their activation rows and packed weights in L2.
-// Split-K: block (tile, split) computes a contiguous range of stages; with
-// S > 1 it stores fp32 partials [split][M][N] and a second kernel adds them in
-// split order.
+// Split-K: block (tile, split) computes a contiguous range of stages and
+// stores fp32 partials [split][tile][BM x BN]; a second kernel adds them in
+// split order.  With few tiles every tile is split; with more tiles than CUs
+// the full rounds take whole tiles and only the last, partial round's tiles
+// are split over the CUs that round would leave idle.
 #include "w4v_device.h"
 #include "w4v_launch.h"
 
@@ -66,6 +68,17 @@ struct Lds {
   static_assert(kBytes <= kLdsLimit, "LDS layout exceeds the block's LDS");
 };
 
+// raster: tile index -> (row block, column block), in groups of kGroupM row
+// blocks with the column blocks inside a group
+__device__ __forceinline__ void tile_coords(int tile, int mblocks, int nblocks, int& mblk,
+                                            int& nblk) {
+  const int per_group = kGroupM * nblocks;
+  const int m_first = tile / per_group * kGroupM;
+  const int gm = mblocks - m_first < kGroupM ? mblocks - m_first : kGroupM;
+  mblk = m_first + (tile % per_group) % gm;
+  nblk = (tile % per_group) / gm;
+}
+
 // s_waitcnt immediate that waits for vmcnt <= n and nothing else (gfx9 field layout)
 constexpr int vmcnt_only(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 constexpr uint32_t kNoMem = 0x80000000u;            // past every resource: reads no memory
@@ -89,9 +102,14 @@ __device__ __forceinline__ u32x4 dequant_natural(uint32_t w, f16x2 z1024, f16x2 
 // Q = 1: group size 128, 4: group size 32.  MTW 16-row m-tiles per wave: block
 // tiles of 32 MTW rows (256, or 192 / 128 for blocks of fewer rows, which then
 // spend no MFMAs and no activation reads on rows that do not exist).
+// Blocks 0 .. dp-1 take whole tiles over all of K (stored as fp16); the
+// blocks after them split each remaining tile dp + u over S contiguous stage
+// ranges (block dp + split * ntail + u) and store fp32 partials
+// [split][u][BM x BN] for the reduce kernel.
 template <int Q, int MTW>
 __global__ __launch_bounds__(kThreads) void w4a16_mfma_kernel(GemmArgs a, int mblocks, int nblocks,
-                                                              int S, float* partials) {
+                                                              int dp, int ntail, int S,
+                                                              float* partials) {
   constexpr int BM = 32 * MTW;
   using L = Lds<MTW>;
   constexpr int kSlots = L::kSlots, kAhead = L::kAhead;
@@ -105,19 +123,18 @@ __global__ __launch_bounds__(kThreads) void w4a16_mfma_kernel(GemmArgs a, int mb
   const int wm = wave & 1, wn = wave >> 1;          // 2 x 4 waves
   const int l16 = lane & 15, kb = lane >> 4;
 
-  // raster: groups of kGroupM row blocks, column blocks inside a group
   const int bid = blockIdx.x;
-  const int per_group = kGroupM * nblocks;
-  const int grp = bid / per_group;
-  const int m_first = grp * kGroupM;
-  const int gm = mblocks - m_first < kGroupM ? mblocks - m_first : kGroupM;
-  const int mblk = m_first + (bid % per_group) % gm;
-  const int nblk = (bid % per_group) / gm;
+  const bool whole = bid < dp;
+  // split tiles in split-major order: the blocks of one stage range run together
+  const int tile = whole ? bid : dp + (bid - dp) % ntail;
+  const int split = whole ? 0 : (bid - dp) / ntail;
+  const int nsplit = whole ? 1 : S;
+  int mblk, nblk;
+  tile_coords(tile, mblocks, nblocks, mblk, nblk);
   const int m0 = mblk * BM, n0 = nblk * BN;
   const int M = a.M, N = a.N;
-  const int split = blockIdx.y;
   const int stages = a.K / BK;
-  const int s_lo = stages * split / S, s_hi = stages * (split + 1) / S;
+  const int s_lo = stages * split / nsplit, s_hi = stages * (split + 1) / nsplit;
 
   const uint32_t lds0 = (uint32_t)reinterpret_cast<uintptr_t>(
       (__attribute__((address_space(3))) unsigned char*)lds);
@@ -283,16 +300,16 @@ __global__ __launch_bounds__(kThreads) void w4a16_mfma_kernel(GemmArgs a, int mb
   // ---- epilogue: lane holds rows 16 mt + 4 kb + e, columns 4 l16 .. + 3 of its tile
   const int col = n0 + wn * 64 + 4 * l16;
   if (col >= N) return;                             // N % 8 == 0: 4 columns all in or all out
-  if (S > 1) {
-    float* pp = partials + (size_t)split * M * N;
+  if (!whole) {
+    float* pp = partials + ((size_t)split * ntail + (tile - dp)) * BM * BN + (col - n0);
 #pragma unroll
     for (int mt = 0; mt < MTW; ++mt)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int m = m0 + wm * 16 * MTW + mt * 16 + 4 * kb + e;
-        if (m < M) {
+        const int r = wm * 16 * MTW + mt * 16 + 4 * kb + e;
+        if (m0 + r < M) {
           const f32x4 val = {acc[mt][0][e], acc[mt][1][e], acc[mt][2][e], acc[mt][3][e]};
-          *reinterpret_cast<f32x4*>(pp + (size_t)m * N + col) = val;
+          *reinterpret_cast<f32x4*>(pp + (size_t)r * BN) = val;
         }
       }
     return;
@@ -311,21 +328,30 @@ __global__ __launch_bounds__(kThreads) void w4a16_mfma_kernel(GemmArgs a, int mb
     }
 }
 
-// y = fp16(alpha * sum of the S partials in split order), 4 columns per thread
+// y = fp16(alpha * sum of the S partials in split order) over the split
+// tiles, 4 columns per thread; BM / 4 blocks of 256 threads per tile
 __global__ __launch_bounds__(256) void w4a16_mfma_reduce_kernel(const float* __restrict__ partials,
                                                                 int S, int M, int N, float alpha,
                                                                 _Float16* __restrict__ y,
-                                                                int64_t ldy) {
-  const size_t i = ((size_t)blockIdx.x * 256 + threadIdx.x) * 4;
-  const size_t total = (size_t)M * N;
-  if (i >= total) return;
+                                                                int64_t ldy, int BM, int mblocks,
+                                                                int nblocks, int dp, int ntail) {
+  const int per_tile = BM / 4;
+  const int u = blockIdx.x / per_tile;
+  const int q = (blockIdx.x % per_tile) * 256 + threadIdx.x;   // quad within the tile
+  const int r = q / (BN / 4), c = (q % (BN / 4)) * 4;
+  int mblk, nblk;
+  tile_coords(dp + u, mblocks, nblocks, mblk, nblk);
+  const int m = mblk * BM + r, n = nblk * BN + c;
+  if (m >= M || n >= N) return;                     // N % 8 == 0: 4 columns all in or all out
+  const size_t tile_elems = (size_t)BM * BN;
+  const size_t i = (size_t)u * tile_elems + (size_t)r * BN + c;
   f32x4 s = *reinterpret_cast<const f32x4*>(partials + i);
-  for (int k = 1; k < S; ++k) s += *reinterpret_cast<const f32x4*>(partials + (size_t)k * total + i);
-  const size_t m = i / N, n = i - m * N;
+  for (int k = 1; k < S; ++k)
+    s += *reinterpret_cast<const f32x4*>(partials + (size_t)k * ntail * tile_elems + i);
   const f16x2 lo = {(_Float16)(alpha * s[0]), (_Float16)(alpha * s[1])};
   const f16x2 hi = {(_Float16)(alpha * s[2]), (_Float16)(alpha * s[3])};
-  *reinterpret_cast<u32x2*>(y + m * ldy + n) = u32x2{__builtin_bit_cast(uint32_t, lo),
-                                                     __builtin_bit_cast(uint32_t, hi)};
+  *reinterpret_cast<u32x2*>(y + (size_t)m * ldy + n) = u32x2{__builtin_bit_cast(uint32_t, lo),
+                                                             __builtin_bit_cast(uint32_t, hi)};
 }
 
 template <int MTW>
@@ -333,10 +359,10 @@ void launch_m(const GemmArgs& a, const MfmaPlan& p, dim3 grid, float* partials,
               hipStream_t stream) {
   if (a.group_size == 32)
     hipLaunchKernelGGL((w4a16_mfma_kernel<4, MTW>), grid, dim3(kThreads), 0, stream, a, p.mblocks,
-                       p.nblocks, p.splits, partials);
+                       p.nblocks, p.dp, p.ntail, p.splits, partials);
   else
     hipLaunchKernelGGL((w4a16_mfma_kernel<1, MTW>), grid, dim3(kThreads), 0, stream, a, p.mblocks,
-                       p.nblocks, p.splits, partials);
+                       p.nblocks, p.dp, p.ntail, p.splits, partials);
 }
 
 }  // namespace
@@ -351,34 +377,63 @@ MfmaPlan plan_w4a16_mfma(int M, int N, int K, int num_cus) {
   const int tiles = p.mblocks * p.nblocks;
   const int stages = K / BK;
   // time ~ rounds of blocks (one block per CU) x stages per block (~0.5 us
-  // each), plus for S > 1 the partials written and read again (2 S M N fp32
+  // each), plus for split tiles their partials written and read again (fp32
   // at ~5 TB/s) and the reduce launch
-  double best = 0;
+  p.dp = tiles;
   p.splits = 1;
-  for (int S = 1; S <= 32 && stages / S >= 8; ++S) {
-    const double rounds = (double)((tiles * S + num_cus - 1) / num_cus);
-    double t = rounds * ((stages + S - 1) / S) * 0.5;
-    if (S > 1) t += 2.0 * S * M * (double)N * 4 / 5e6 + 3.0;
-    if (S == 1 || t < best - 1e-9) {
-      best = t;
-      p.splits = S;
+  const double tile_bytes = (double)BM * BN * 4;
+  if (tiles <= num_cus) {
+    // few tiles: every tile split S ways
+    double best = 0;
+    for (int S = 1; S <= 32 && stages / S >= 8; ++S) {
+      const double rounds = (double)((tiles * S + num_cus - 1) / num_cus);
+      double t = rounds * ((stages + S - 1) / S) * 0.5;
+      if (S > 1) t += 2.0 * S * M * (double)N * 4 / 5e6 + 3.0;
+      if (S == 1 || t < best - 1e-9) {
+        best = t;
+        p.splits = S;
+        p.dp = S > 1 ? 0 : tiles;
+      }
+    }
+  } else if (tiles % num_cus != 0) {
+    // whole tiles for the full rounds, and the last partial round's tiles
+    // split over the CUs that round would leave idle (M = 2048 gate+up: 608
+    // tiles = 2 rounds + 96 tiles x 2 splits instead of 3 rounds)
+    // (a full-size tile's stage takes ~1 us with a CU to itself, measured on
+    // MI355X at 2048 and 8192 rows)
+    const int full = tiles / num_cus, rem = tiles % num_cus;
+    int st = num_cus / rem;
+    while (st > 1 && stages / st < 8) --st;
+    if (st > 1) {
+      const double stage_us = 1.0;
+      const double t_whole = (full + 1) * stages * stage_us;
+      const double t_tail = full * stages * stage_us + ((stages + st - 1) / st) * stage_us +
+                            2.0 * st * rem * tile_bytes / 5e6 + 3.0;
+      if (t_tail < t_whole) {
+        p.dp = full * num_cus;
+        p.splits = st;
+      }
     }
   }
-  p.partial_bytes = p.splits > 1 ? (size_t)p.splits * M * N * sizeof(float) : 0;
+  p.ntail = p.splits > 1 ? tiles - p.dp : 0;
+  p.partial_bytes = p.splits > 1 ? (size_t)p.splits * p.ntail * (size_t)BM * BN * sizeof(float) : 0;
   return p;
 }
 
 hipError_t launch_w4a16_mfma(const GemmArgs& a, const MfmaPlan& p, float* partials,
                              hipStream_t stream) {
-  const dim3 grid(p.mblocks * p.nblocks, p.splits);
+  if (p.dp + p.ntail != p.mblocks * p.nblocks || (p.splits > 1) != (p.ntail > 0))
+    return hipErrorInvalidValue;
+  const dim3 grid(p.dp + p.ntail * p.splits);
   if (p.mtw == 8) launch_m<8>(a, p, grid, partials, stream);
   else if (p.mtw == 6) launch_m<6>(a, p, grid, partials, stream);
   else if (p.mtw == 4) launch_m<4>(a, p, grid, partials, stream);
   else return hipErrorInvalidValue;
-  if (p.splits > 1) {
-    const size_t quads = ((size_t)a.M * a.N + 3) / 4;
-    hipLaunchKernelGGL(w4a16_mfma_reduce_kernel, dim3((unsigned)((quads + 255) / 256)), dim3(256),
-                       0, stream, partials, p.splits, a.M, a.N, a.alpha, a.y, a.ldy);
+  if (p.ntail > 0) {
+    const int bm = 32 * p.mtw;
+    hipLaunchKernelGGL(w4a16_mfma_reduce_kernel, dim3((unsigned)(p.ntail * (bm / 4))), dim3(256),
+                       0, stream, partials, p.splits, a.M, a.N, a.alpha, a.y, a.ldy, bm,
+                       p.mblocks, p.nblocks, p.dp, p.ntail);
   }
   return hipGetLastError();
 }

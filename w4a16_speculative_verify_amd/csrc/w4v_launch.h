@@ -64,8 +64,10 @@ constexpr int kMfmaMinRows = 33;
 struct MfmaPlan {
   int mtw;               // 16-row m-tiles per wave: block tiles of 32 mtw rows x 256 columns
   int mblocks, nblocks;
-  int splits;            // K-splits (1 = none)
-  size_t partial_bytes;  // fp32 [splits][M][N] when splits > 1
+  int dp;                // tiles computed whole (the first dp of the raster order)
+  int ntail;             // tiles after them, each split `splits` ways (0 when splits == 1)
+  int splits;            // K-splits of the tail tiles (1 = none)
+  size_t partial_bytes;  // fp32 [splits][ntail][32 mtw x 256] when splits > 1
 };
 MfmaPlan plan_w4a16_mfma(int M, int N, int K, int num_cus);
 hipError_t launch_w4a16_mfma(const GemmArgs& a, const MfmaPlan& p, float* partials,
