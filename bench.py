@@ -770,45 +770,50 @@ def main():
         drafts_all[i], r = gen.make_drafts(drng, cfg, t_host)
         planned[i] = r[0]
     drafts_dev = up(drafts_all)
-    drafts_buf = torch.empty((1, cfg.k_draft), dtype=torch.int32, device=dev)
     acc_hist = torch.zeros(total, dtype=torch.int32, device=dev)
 
-    # capture: the whole step, and the linears alone (roofline timing)
+    # every step reads its own drafts and writes its own accepted length in HBM
+    # (as a drafter running on the device leaves them); the warm-up steps run
+    # eagerly, the timed ones from HIP graphs of `chunk` consecutive steps, with
+    # an event between graphs (per-step times: each graph's time / its steps)
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
-        step(x, drafts_buf)
+        for i in range(args.warmup):
+            step(x, drafts_dev[i], accepted_len=acc_hist[i:i + 1])
     torch.cuda.current_stream().wait_stream(s)
     torch.cuda.synchronize()
-    g_step = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g_step):
-        step(x, drafts_buf)
+    chunk = 10
+    starts = list(range(args.warmup, total, chunk))
+    sizes = [min(chunk, total - c0) for c0 in starts]
+    graphs = []
+    for c0, n_c in zip(starts, sizes):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(c0, c0 + n_c):
+                step(x, drafts_dev[i], accepted_len=acc_hist[i:i + 1])
+        graphs.append(g)
+    # the linears alone (roofline timing)
     g_lin = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g_lin):
         step.linears_only(x)
+    for g in graphs:                                # first replays: untimed
+        g.replay()
     torch.cuda.synchronize()
-
-    def one_step(i):
-        drafts_buf.copy_(drafts_dev[i], non_blocking=True)
-        g_step.replay()
-        acc_hist[i:i + 1].copy_(step.accepted_len, non_blocking=True)
-
-    for i in range(args.warmup):
-        one_step(i)
-    torch.cuda.synchronize()
+    acc_hist[args.warmup:].zero_()
 
     stream = torch.cuda.current_stream()
-    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(len(graphs) + 1)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     evs[0].record(stream)
-    for j, i in enumerate(range(args.warmup, total)):
-        one_step(i)
+    for j, g in enumerate(graphs):
+        g.replay()
         evs[j + 1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     step_ms = evs[0].elapsed_time(evs[-1]) / args.steps
-    per_step = np.array([evs[j].elapsed_time(evs[j + 1]) for j in range(args.steps)])
+    per_step = np.array([evs[j].elapsed_time(evs[j + 1]) / sizes[j] for j in range(len(graphs))])
     p10, p50, p90 = (float(np.percentile(per_step, q)) for q in (10, 50, 90))
 
     acc = acc_hist.cpu().numpy().astype(np.int64)
@@ -858,7 +863,7 @@ def main():
     pre = None
     if not args.no_prefill:
         print("[bench] timing the prefill-shaped linears", file=sys.stderr, flush=True)
-        del g_step, g_lin
+        del graphs, g_lin
         pre = prefill(dev)
 
     commit = None
