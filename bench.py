@@ -311,26 +311,22 @@ def g32_target(dev, steps: int = 50, warmup: int = 5):
                                               gen.draw_r_geometric(rng, tg.k_draft))
                        for _ in range(total)])[:, None, :]
     drafts_dev = up(drafts.astype(np.int32))
-    buf = torch.empty((1, tg.k_draft), dtype=torch.int32, device=dev)
     acc_hist = torch.zeros(total, dtype=torch.int32, device=dev)
-    step(x, buf)
+    # as the main step: each step reads its own drafts and writes its own
+    # accepted length; warm-up eagerly, the timed steps from one HIP graph
+    for i in range(warmup):
+        step(x, drafts_dev[i], accepted_len=acc_hist[i:i + 1])
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
-        step(x, buf)
-
-    def one(i):
-        buf.copy_(drafts_dev[i], non_blocking=True)
-        g.replay()
-        acc_hist[i:i + 1].copy_(step.accepted_len, non_blocking=True)
-
-    for i in range(warmup):
-        one(i)
+        for i in range(warmup, total):
+            step(x, drafts_dev[i], accepted_len=acc_hist[i:i + 1])
+    g.replay()
     torch.cuda.synchronize()
+    acc_hist[warmup:].zero_()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
-    for i in range(warmup, total):
-        one(i)
+    g.replay()
     e1.record()
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / steps
