@@ -25,7 +25,9 @@
 //            dropped for one-tile blocks, 1,173 -> 1,150 us at M = 16; direct
 //            fragments at M = 1, 1,081 -> 1,060 us (at M = 16 they touch 16
 //            rows per instruction and were slower, 1,179 us).
-// Loads run D groups ahead of the math (a ring of register sets), and every
+// Loads run D groups ahead of the math (a ring of register sets; the plans
+// use D = 2, which beat 3 at every shape on MI355X: a third slot mostly
+// issues empty loads ahead of the first step and holds registers), and every
 // load is unconditional (a missing group reads zeros from outside its buffer
 // resource), because a load under a branch makes the compiler wait for all
 // loads in flight.
