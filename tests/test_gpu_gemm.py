@@ -230,6 +230,9 @@ def test_prefill_full_output(lib, m, shape):
     (512, 384, 136),           # ragged N
     (600, 1280, 1032),
     (1000, 128, 8),            # one group, narrowest N
+    # 3 x 89 = 267 tiles on 256 CUs: 256 whole tiles, the last 11 split 8 ways, ragged
+    # rows (88 of the last row block) and columns (8 of the last column block)
+    (600, 2048, 22536),
 ])
 def test_mfma_path_shapes(lib, m, k, n):
     log(f"gemm m={m} k={k} n={n}")
