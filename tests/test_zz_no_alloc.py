@@ -29,6 +29,8 @@ def _pair(w4v, x, lin, alpha):
     ((16, 9728, 2560), (3, 128, 8)),
     # the M >= 33 kernel with K-split partials in the scratch, then a smaller split plan
     ((168, 2560, 6144), (40, 1280, 136)),
+    # whole tiles plus a split tail (256 + 11 x 8), then a fully split plan
+    ((600, 2048, 22536), (40, 1280, 136)),
 ])
 def test_noalloc_matches_workspace_entry_point(lib, shapes):
     for i, (m, k, n) in enumerate(shapes):
