@@ -97,19 +97,21 @@ int w4v_read_probe(const void* src, size_t bytes, uint32_t* out, void* stream);
  *          scale applied to that group's fp32 sum (split-K across blocks).
  *          M >= 33 (the batched verify block, prefill shapes: bound by the
  *          matrix cores): an LDS-tiled MFMA kernel that dequantises each
- *          256-column x 32-k weight tile once per 256-row block tile, as
- *          w = fp16_rne(s * (q - z)) (q - z exact, one rounding; the fp32
- *          accumulation and the alpha / output rounding as above); shapes with
- *          few block tiles are split along K with fp32 partials in the
- *          workspace, added in split order by a second kernel.  The plan (and
- *          so the result) depends on the shape alone.
+ *          256-column x 32-k weight tile once per block tile of 256 rows (128
+ *          or 192 for calls with no more rows), as w = fp16_rne(s * (q - z))
+ *          (q - z exact, one rounding; the fp32 accumulation and the alpha /
+ *          output rounding as above); shapes with fewer block tiles than CUs
+ *          are split along K, and with more, the tiles of the last partial
+ *          round are, with fp32 partials in the workspace added in split
+ *          order by a second kernel.  The plan (and so the result) depends on
+ *          the shape alone.
  * workspace  device memory of at least w4a16_gemm_workspace_size(M, N, K,
  *          group_size) bytes (may be NULL when that size is 0), 256-byte
  *          aligned, zeroed once by the caller.  Its first 64 KiB hold the
  *          split-K arrival counters of the M <= 32 path (every call leaves them
  *          at zero), the next 4 MiB at most that path's fp32 partial sums; the
- *          M >= 33 path's fp32 partials [splits x M x N] come after those
- *          4 MiB.  A workspace smaller than the query's size (NULL included)
+ *          M >= 33 path's fp32 partials [splits x split tiles x tile rows x
+ *          256] come after those 4 MiB.  A workspace smaller than the query's size (NULL included)
  *          returns W4V_ERR_WORKSPACE.  Partials are added in split order, so
  *          the result does not depend on the order in which they arrive.  One
  *          workspace sized for the largest call serves calls of every shape
