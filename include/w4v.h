@@ -117,9 +117,11 @@ int w4v_read_probe(const void* src, size_t bytes, uint32_t* out, void* stream);
  *          workspace sized for the largest call serves calls of every shape
  *          ordered on one stream.
  * Placement  the first M <= 32 call with a K-split on a device, outside
- *          stream capture, launches a small probe of how the device deals
- *          blocks to its XCDs and waits for `stream` once; when blocks whose
- *          ids agree mod 8 share an XCD, later calls keep the split-K
+ *          stream capture, enqueues on `stream` a small probe of how the
+ *          device deals blocks to its XCDs (with a copy of its one-word result
+ *          to pinned host memory and an event; nothing waits for them); when a
+ *          later call outside capture finds the probe done and blocks whose
+ *          ids agree mod 8 share an XCD, it and later calls keep the split-K
  *          hand-off in that XCD's L2 (same result bits either way).
  * ---------------------------------------------------------------------- */
 size_t w4a16_gemm_workspace_size(int M, int N, int K, int group_size);

@@ -556,29 +556,60 @@ GemmPlan plan_w4a16(int M, int N, int K, int num_cus) {
 
 namespace {
 std::mutex g_probe_mu;
-int g_xcd_state[64];    // per device: 0 not probed, 1 round-robin placement, 2 not
+// per device: 0 not probed, 1 probe in flight, 2 round-robin placement, 3 not
+// (or the probe could not run)
+int g_xcd_state[64];
+hipEvent_t g_xcd_event[64];
+unsigned* g_xcd_host[64];    // pinned word the probe's result is copied to
 }  // namespace
 
 // Whether blocks with ids equal mod 8 share an XCD on the current device.  The
-// first call outside stream capture runs the probe on `stream` and waits for
-// it (once per device); until then, and under capture, the answer is no.
+// first call outside stream capture enqueues the probe, a copy of its result
+// to pinned host memory and an event on `stream`, and never waits for them; a
+// later call outside capture that finds the event complete reads the result.
+// Until then, and under capture, the answer is no (the memory-side hand-off,
+// same result bits).
 static bool xcd_round_robin(hipStream_t stream) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return false;
   std::lock_guard<std::mutex> lock(g_probe_mu);
-  if (g_xcd_state[dev] == 0) {
+  int& st = g_xcd_state[dev];
+  if (st == 0 || st == 1) {
     hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
     if (hipStreamIsCapturing(stream, &cap) != hipSuccess || cap != hipStreamCaptureStatusNone)
       return false;
-    unsigned mask = 0u;
-    hipLaunchKernelGGL(xcd_probe_kernel, dim3(256), dim3(64), 0, stream);
-    if (hipGetLastError() != hipSuccess || hipStreamSynchronize(stream) != hipSuccess ||
-        hipMemcpyFromSymbol(&mask, HIP_SYMBOL(g_xcd_offsets), sizeof(mask), 0,
-                            hipMemcpyDeviceToHost) != hipSuccess)
-      return false;
-    g_xcd_state[dev] = (mask != 0u && (mask & (mask - 1u)) == 0u) ? 1 : 2;
   }
-  return g_xcd_state[dev] == 1;
+  if (st == 0) {
+    void* sym = nullptr;
+    if (hipHostMalloc(reinterpret_cast<void**>(&g_xcd_host[dev]), sizeof(unsigned),
+                      hipHostMallocDefault) != hipSuccess ||
+        hipEventCreateWithFlags(&g_xcd_event[dev], hipEventDisableTiming) != hipSuccess ||
+        hipGetSymbolAddress(&sym, HIP_SYMBOL(g_xcd_offsets)) != hipSuccess) {
+      st = 3;
+      return false;
+    }
+    hipLaunchKernelGGL(xcd_probe_kernel, dim3(256), dim3(64), 0, stream);
+    if (hipGetLastError() != hipSuccess ||
+        hipMemcpyAsync(g_xcd_host[dev], sym, sizeof(unsigned), hipMemcpyDeviceToHost, stream) !=
+            hipSuccess ||
+        hipEventRecord(g_xcd_event[dev], stream) != hipSuccess) {
+      st = 3;
+      return false;
+    }
+    st = 1;
+    return false;
+  }
+  if (st == 1) {
+    const hipError_t q = hipEventQuery(g_xcd_event[dev]);
+    if (q == hipErrorNotReady) return false;
+    if (q != hipSuccess) {
+      st = 3;
+      return false;
+    }
+    const unsigned mask = *g_xcd_host[dev];
+    st = (mask != 0u && (mask & (mask - 1u)) == 0u) ? 2 : 3;
+  }
+  return st == 2;
 }
 
 hipError_t launch_w4a16_skinny(const GemmArgs& a, const GemmPlan& p, void* workspace,
