@@ -146,7 +146,10 @@ int w4a16_gemm(const void* x, int64_t ldx,
  * (also when captured); the kernels re-arm it after every call.
  * Calls on one GPU share the array: two calls whose executions overlap on
  * one GPU (different streams, or graphs replayed concurrently) race, so
- * order them on one stream.  Never calls hipMalloc or hipFree.
+ * order them on one stream.  Never calls hipMalloc, hipFree or any other
+ * allocating routine: it never starts the XCD placement probe (whose result
+ * word is pinned host memory), and keeps the split-K hand-off on the memory
+ * side until a w4a16_gemm call's probe result is known.
  * ---------------------------------------------------------------------- */
 #define W4V_STATIC_SCRATCH_BYTES (32u << 20)
 

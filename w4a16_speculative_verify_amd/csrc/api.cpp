@@ -370,9 +370,11 @@ size_t w4a16_gemm_workspace_size(int M, int N, int K, int group_size) {
   return w4v::plan_w4a16(M, N, K, kPlanCUs).workspace_bytes();
 }
 
-int w4a16_gemm(const void* x, int64_t ldx, const int32_t* qweight, const void* scales,
-               const int32_t* qzeros, void* y, int64_t ldy, int M, int N, int K, int group_size,
-               float alpha, void* workspace, size_t workspace_bytes, void* stream) {
+// w4a16_gemm; may_probe = false for the entry point that must not allocate
+static int gemm_impl(const void* x, int64_t ldx, const int32_t* qweight, const void* scales,
+                     const int32_t* qzeros, void* y, int64_t ldy, int M, int N, int K,
+                     int group_size, float alpha, void* workspace, size_t workspace_bytes,
+                     void* stream, bool may_probe) {
   int st = gemm_check(x, ldx, qweight, scales, qzeros, y, ldy, M, N, K, group_size);
   if (st != W4V_OK || M == 0 || N == 0) return st;
   // buffer resources take 32-bit offsets below 2 GiB
@@ -412,8 +414,15 @@ int w4a16_gemm(const void* x, int64_t ldx, const int32_t* qweight, const void* s
     return W4V_ERR_UNSUPPORTED;
   st = workspace_check(p.workspace_bytes(), workspace, workspace_bytes);
   if (st != W4V_OK) return st;
-  hipError_t e = w4v::launch_w4a16_skinny(a, p, workspace, s);
+  hipError_t e = w4v::launch_w4a16_skinny(a, p, workspace, s, may_probe);
   return e == hipSuccess ? W4V_OK : W4V_ERR_HIP;
+}
+
+int w4a16_gemm(const void* x, int64_t ldx, const int32_t* qweight, const void* scales,
+               const int32_t* qzeros, void* y, int64_t ldy, int M, int N, int K, int group_size,
+               float alpha, void* workspace, size_t workspace_bytes, void* stream) {
+  return gemm_impl(x, ldx, qweight, scales, qzeros, y, ldy, M, N, K, group_size, alpha, workspace,
+                   workspace_bytes, stream, true);
 }
 
 int w4a16_gemm_noalloc(const void* x, int64_t ldx, const int32_t* qweight, const void* scales,
@@ -428,8 +437,8 @@ int w4a16_gemm_noalloc(const void* x, int64_t ldx, const int32_t* qweight, const
     st = scratch_for_current_device(static_cast<hipStream_t>(stream), &ws);
     if (st != W4V_OK) return st;
   }
-  return w4a16_gemm(x, ldx, qweight, scales, qzeros, y, ldy, M, N, K, group_size, alpha, ws,
-                    ws ? (size_t)W4V_STATIC_SCRATCH_BYTES : 0, stream);
+  return gemm_impl(x, ldx, qweight, scales, qzeros, y, ldy, M, N, K, group_size, alpha, ws,
+                   ws ? (size_t)W4V_STATIC_SCRATCH_BYTES : 0, stream, false);
 }
 
 size_t w8a16_lmhead_argmax_workspace_size(int M, int H, int V) {

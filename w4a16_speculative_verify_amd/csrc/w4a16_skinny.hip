@@ -568,12 +568,14 @@ unsigned* g_xcd_host[64];    // pinned word the probe's result is copied to
 // to pinned host memory and an event on `stream`, and never waits for them; a
 // later call outside capture that finds the event complete reads the result.
 // Until then, and under capture, the answer is no (the memory-side hand-off,
-// same result bits).
-static bool xcd_round_robin(hipStream_t stream) {
+// same result bits).  may_probe = false (callers that must not allocate: the
+// probe's host word is pinned memory) only reads a result another call started.
+static bool xcd_round_robin(hipStream_t stream, bool may_probe) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return false;
   std::lock_guard<std::mutex> lock(g_probe_mu);
   int& st = g_xcd_state[dev];
+  if (st == 0 && !may_probe) return false;
   if (st == 0 || st == 1) {
     hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
     if (hipStreamIsCapturing(stream, &cap) != hipSuccess || cap != hipStreamCaptureStatusNone)
@@ -613,13 +615,13 @@ static bool xcd_round_robin(hipStream_t stream) {
 }
 
 hipError_t launch_w4a16_skinny(const GemmArgs& a, const GemmPlan& p, void* workspace,
-                               hipStream_t stream) {
+                               hipStream_t stream, bool may_probe) {
   unsigned* tickets = nullptr;
   float* partials = nullptr;
   GemmArgs la = a;
   la.xcd_local = 0;
   if (p.splits > 1) {
-    la.xcd_local = xcd_round_robin(stream) ? 1 : 0;
+    la.xcd_local = xcd_round_robin(stream, may_probe) ? 1 : 0;
     tickets = static_cast<unsigned*>(workspace);
     partials = reinterpret_cast<float*>(static_cast<char*>(workspace) + p.ticket_bytes);
   }

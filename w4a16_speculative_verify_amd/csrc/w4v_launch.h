@@ -55,7 +55,7 @@ struct GemmPlan {
 
 GemmPlan plan_w4a16(int M, int N, int K, int num_cus);
 hipError_t launch_w4a16_skinny(const GemmArgs& a, const GemmPlan& p, void* workspace,
-                               hipStream_t stream);
+                               hipStream_t stream, bool may_probe = true);
 
 // From this many rows on: the LDS-tiled MFMA kernel (weights dequantised once
 // per 256 x 256 block tile into LDS), split-K with fp32 partials in the
