@@ -121,8 +121,10 @@ int w4v_read_probe(const void* src, size_t bytes, uint32_t* out, void* stream);
  *          device deals blocks to its XCDs (with a copy of its one-word result
  *          to pinned host memory and an event; nothing waits for them); when a
  *          later call outside capture finds the probe done and blocks whose
- *          ids agree mod 8 share an XCD, it and later calls keep the split-K
- *          hand-off in that XCD's L2 (same result bits either way).
+ *          ids agree mod 8 share an XCD, it and later calls pass the split-K
+ *          partials with plain stores and L1-missing loads instead of
+ *          device-coherent (sc1) ones, valid because every split of a tile
+ *          then runs on one XCD (same result bits either way).
  * ---------------------------------------------------------------------- */
 size_t w4a16_gemm_workspace_size(int M, int N, int K, int group_size);
 

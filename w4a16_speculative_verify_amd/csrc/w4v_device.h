@@ -160,10 +160,11 @@ __device__ __forceinline__ u32x4 ld_agent_x4(rsrc_t r, uint32_t off) {
   return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kSC1);
 }
 
-// The same hand-off kept in one XCD's L2, for blocks known to share it:
-// plain stores (written through the vector L1 into the L2) and loads with the
-// sc0 bit (they miss the L1 and read the L2).  Valid only when every block
-// that writes or reads the partials runs on the same XCD.
+// The same hand-off for blocks known to share one XCD's L2: plain stores
+// (written through the vector L1 into the L2) and loads with the sc0 bit
+// (they miss the L1).  Valid only when every block that writes or reads the
+// partials runs on the same XCD.  It saves the sc1 round trips; by the
+// fetch counters the partials still travel to and from the memory side.
 constexpr int kSC0 = 1;
 
 // Block barrier that orders LDS accesses only.  __syncthreads() also waits
