@@ -132,18 +132,30 @@ def drafter_cpu():
 def counter_traffic():
     """HBM bytes per W4A16 launch from the committed counter summary, or None
     when the kernel sources have changed since the counters were taken."""
-    import hashlib
     path = os.path.join(ROOT, "profiles", "w4a16_skinny_traffic.json")
     try:
         with open(path) as f:
             rec = json.load(f)
-        h = hashlib.sha256()
-        for src in rec["sources"]:
-            with open(os.path.join(ROOT, src), "rb") as f:
-                h.update(f.read())
+        digest = source_digest(rec["sources"])
     except (OSError, KeyError, ValueError):
         return None
-    return rec["traffic_bytes_per_launch"] if h.hexdigest() == rec["sha256"] else None
+    return rec["traffic_bytes_per_launch"] if digest == rec["sha256"] else None
+
+
+def source_digest(sources):
+    """sha256 over the given sources with comments removed and whitespace
+    collapsed, so that a change of wording does not mark the counters stale
+    (code changes do)."""
+    import hashlib
+    import re
+    h = hashlib.sha256()
+    for src in sources:
+        with open(os.path.join(ROOT, src)) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", "", text)
+        h.update(" ".join(text.split()).encode())
+    return h.hexdigest()
 
 
 def device_info(dev):
