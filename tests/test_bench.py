@@ -50,7 +50,7 @@ def test_counter_traffic_guard(tmp_path, monkeypatch):
     rec_path = os.path.join(ROOT, "profiles", "w4a16_skinny_traffic.json")
     rec = json.load(open(rec_path))
     assert bench.counter_traffic() in (rec["traffic_bytes_per_launch"], None)
-    # a copy of the tree whose kernel source differs by one byte: the record is dropped
+    # a copy of the tree whose kernel code changes: the record is dropped
     fake = tmp_path / "root"
     (fake / "profiles").mkdir(parents=True)
     (fake / "profiles" / "w4a16_skinny_traffic.json").write_text(json.dumps(rec))
@@ -63,5 +63,10 @@ def test_counter_traffic_guard(tmp_path, monkeypatch):
         pytest.skip("the working tree's kernel sources differ from the recorded ones")
     assert bench.counter_traffic() == rec["traffic_bytes_per_launch"]
     first = fake / rec["sources"][0]
-    first.write_bytes(first.read_bytes() + b" ")
+    code = first.read_bytes()
+    # comments and whitespace do not count
+    first.write_bytes(code + b"\n// a comment\n/* another */  \n")
+    assert bench.counter_traffic() == rec["traffic_bytes_per_launch"]
+    # one more token of code does
+    first.write_bytes(code + b";")
     assert bench.counter_traffic() is None
