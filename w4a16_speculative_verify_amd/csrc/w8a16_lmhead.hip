@@ -85,11 +85,18 @@ __global__ __launch_bounds__(64 * NW) void lmhead_argmax_kernel(LmheadArgs a, un
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int kb = lane >> 4;
-  // grid x = m-blocks, y = vocabulary blocks: the m-blocks of one vocabulary
-  // share are dispatched together and read its weights at about the same time
-  const int vbk = blockIdx.y;
-  const int mbase = blockIdx.x * 16 * MT;
-  const int nvb = gridDim.y;
+  // Four-wave blocks: grid x = m-blocks, y = vocabulary blocks, so that the
+  // m-blocks of one vocabulary share are dispatched together and read its
+  // weights at about the same time (the grid can exceed one block per CU).
+  // Eight-wave blocks (two m-blocks, one block per CU, all resident at once):
+  // x = vocabulary share, so that the two m-blocks of a share (ids v and
+  // v + shares) run on one XCD and share its L2 when the share count is a
+  // multiple of 8 (128 shares for the 151,936-row head).
+  constexpr bool kShareX = NW == 8;
+  const int vbk = kShareX ? blockIdx.x : blockIdx.y;
+  const int mblk = kShareX ? blockIdx.y : blockIdx.x;
+  const int mbase = mblk * 16 * MT;
+  const int nvb = kShareX ? gridDim.x : gridDim.y;
   constexpr int kRowsPerPass = kWaves * TILES * 16;
   // this block's vocabulary rows: an equal share [vb0, vb1), in passes
   const int vb0 = (int)((long long)a.V * vbk / nvb);
@@ -292,7 +299,7 @@ __global__ __launch_bounds__(64 * NW) void lmhead_argmax_kernel(LmheadArgs a, un
   }
   __syncthreads();
   const int nblocks = gridDim.x * gridDim.y;
-  const int bid = blockIdx.x * nvb + vbk;
+  const int bid = mblk * nvb + vbk;
   if (threadIdx.x < R) {
     float v = s_val[0][threadIdx.x];
     int i = s_idx[0][threadIdx.x];
@@ -352,12 +359,14 @@ __global__ __launch_bounds__(64 * NW) void lmhead_argmax_kernel(LmheadArgs a, un
 template <int MT, int TILES, int WH, int NW>
 void launch_h(const LmheadArgs& a, const LmheadPlan& p, unsigned* ticket, float* pval, int* pidx,
               hipStream_t stream) {
+  // grid axes as the kernel reads them (x = vocabulary shares for eight waves)
+  const dim3 grid = NW == 8 ? dim3(p.vblocks, p.mblocks) : dim3(p.mblocks, p.vblocks);
   if (a.f16)
-    hipLaunchKernelGGL((lmhead_argmax_kernel<MT, TILES, 3, 1, WH, NW>),
-                       dim3(p.mblocks, p.vblocks), dim3(64 * NW), 0, stream, a, ticket, pval, pidx);
+    hipLaunchKernelGGL((lmhead_argmax_kernel<MT, TILES, 3, 1, WH, NW>), grid, dim3(64 * NW), 0,
+                       stream, a, ticket, pval, pidx);
   else
-    hipLaunchKernelGGL((lmhead_argmax_kernel<MT, TILES, 3, 0, WH, NW>),
-                       dim3(p.mblocks, p.vblocks), dim3(64 * NW), 0, stream, a, ticket, pval, pidx);
+    hipLaunchKernelGGL((lmhead_argmax_kernel<MT, TILES, 3, 0, WH, NW>), grid, dim3(64 * NW), 0,
+                       stream, a, ticket, pval, pidx);
 }
 
 template <int MT, int TILES>
