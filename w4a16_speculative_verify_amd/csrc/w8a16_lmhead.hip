@@ -42,7 +42,9 @@ namespace w4v {
 namespace {
 
 constexpr int kChunk = 128;                         // k per step
-constexpr int kHRowWords = (kChunk * 2 + 16) / 4;   // padded LDS row of the hidden chunk
+// LDS row of the per-step hidden chunk: 16 chunks of 16 bytes, unpadded; chunk c
+// of row r sits at c ^ hswz(r % 16), as in the whole-row tile
+constexpr int kHRowWords = kChunk * 2 / 4;
 constexpr int kLmheadBlocksPerCU = 1;
 constexpr int kWholeH = 2560;                       // widest hidden row staged whole (16-row blocks)
 
@@ -204,6 +206,9 @@ __global__ __launch_bounds__(64 * NW) void lmhead_argmax_kernel(LmheadArgs a, un
   }
   const int arow = lane & 15;
   const int aswz = hswz(arow);
+  // this thread's chunk position in the per-step tile (its rows are hr + a
+  // multiple of 16, so they share hr % 16)
+  const int hsw = hc ^ hswz(hr & 15);
   // steps padded to a multiple of D: no branch around loads or barriers
   const int nsteps_pad = (nsteps + D - 1) / D * D;
   for (int s0 = 0; s0 < nsteps_pad; s0 += D) {
@@ -214,7 +219,7 @@ __global__ __launch_bounds__(64 * NW) void lmhead_argmax_kernel(LmheadArgs a, un
       if constexpr (!WH) {
 #pragma unroll
         for (int j = 0; j < HR; ++j)
-          *reinterpret_cast<u32x4*>(ht + (j * kRowsPerRound + hr) * kHRowWords + hc * 4) =
+          *reinterpret_cast<u32x4*>(ht + (j * kRowsPerRound + hr) * kHRowWords + hsw * 4) =
               f[i].h[j];
         lds_barrier();
       }
@@ -231,7 +236,7 @@ __global__ __launch_bounds__(64 * NW) void lmhead_argmax_kernel(LmheadArgs a, un
               av[mt] = *reinterpret_cast<const f16x8*>(hseg + (((kb * 4 + q) ^ aswz) * 4));
             else
               av[mt] = *reinterpret_cast<const f16x8*>(ht + (mt * 16 + arow) * kHRowWords +
-                                                       kb * 16 + q * 4);
+                                                       (((kb * 4 + q) ^ aswz) * 4));
           }
 #pragma unroll
           for (int t = 0; t < TILES; ++t) {
